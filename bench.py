@@ -1,0 +1,337 @@
+"""Decode-step benchmark for hybrid-tier decode attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload ctx128k]
+
+A step is one decode step of the whole hot path over one request: for each of
+the 16 attention layers, int8 decode over the old pages, exact BF16 decode
+over the recent window, and the LSE merge of the two tiers.  Inputs (seeded
+synthetic history, drawn on the device; pages quantized with the library's
+own quantizer) are resident in HBM before timing starts.  Alongside the
+hybrid step the same history is decoded all-BF16 (exact tier over every
+page), and the quantizer's throughput is measured separately (it runs off
+the decode path).
+
+Prints ONE JSON line (rank 0).  `value` is KV bytes read per second by the
+hybrid step; µs per step is in `ms_per_step` and `extra`.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+PAGE_INT8_BYTES = 64 * 256 * 2 + 64 * 4 + 256 * 4 * 2  # codes K+V, k_tok, k_chan, v_chan = 35,072
+PAGE_BF16_BYTES = 64 * 256 * 2 * 2  # K+V = 65,536
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("decode.hip", "akv_device.h"):
+        h.update(open(os.path.join(ROOT, "quantized_paged_kv_akv_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def step_kv_bytes(plan, Hkv) -> dict:
+    """Algorithmic KV bytes one decode step reads per layer (codes + FP32
+    scales of the int8 pages, BF16 K and V of the window pages)."""
+    n8 = sum(plan.n8)
+    win_pages = sum((t + 63) // 64 for t in plan.win_tokens)
+    return dict(int8=n8 * Hkv * PAGE_INT8_BYTES, window=win_pages * Hkv * PAGE_BF16_BYTES,
+                bf16_all=sum(plan.n_pages) * Hkv * PAGE_BF16_BYTES)
+
+
+def build_layers(w, device):
+    """Per layer: BF16 pool (whole history), int8 pool of the old pages,
+    tables.  The int8 pool is produced by akv_quantize_pages."""
+    import numpy as np
+    import torch
+
+    from quantized_paged_kv_akv_amd import binding as B
+    from quantized_paged_kv_akv_amd import inputs
+
+    plan = inputs.plan_pools(w)
+    Hkv = w.num_kv_heads
+    dims = B.dims(Hkv, w.group)
+    src, dst = plan.quant_src_dst()
+    src_t = torch.as_tensor(src, device=device)
+    dst_t = torch.as_tensor(dst, device=device)
+    layers = []
+    qt_ms = []
+    for layer in range(w.layers):
+        d = inputs.make_layer_torch(w, layer, device, plan)
+        n8 = plan.int8_slots_total
+        L = dict(q=d["q"], k_pool=d["k_pool"], v_pool=d["v_pool"],
+                 k_codes=torch.empty((n8, Hkv, 64, 256), dtype=torch.int8, device=device),
+                 v_codes=torch.empty((n8, Hkv, 256, 64), dtype=torch.int8, device=device),
+                 k_chan=torch.empty((n8, Hkv, 256), device=device),
+                 k_tok=torch.empty((n8, Hkv, 64), device=device),
+                 v_chan=torch.empty((n8, Hkv, 256), device=device))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        B.akv_quantize_pages(dims, len(src), L["k_pool"], L["v_pool"], src_t, dst_t, L["k_codes"], L["v_codes"],
+                             L["k_chan"], L["k_tok"], L["v_chan"])
+        e1.record()
+        torch.cuda.synchronize()
+        qt_ms.append(e0.elapsed_time(e1))
+        layers.append(L)
+    tables = dict(t8=torch.as_tensor(plan.int8_table(), device=device),
+                  tw=torch.as_tensor(plan.window_table(), device=device),
+                  tf=torch.as_tensor(plan.full_table(), device=device),
+                  n8=torch.as_tensor(np.asarray(plan.n8, np.int32), device=device),
+                  nw=torch.as_tensor(np.asarray(plan.win_tokens, np.int32), device=device),
+                  nf=torch.as_tensor(np.asarray([int(x) for x in w.lengths], np.int32), device=device))
+    return plan, layers, tables, qt_ms, len(src)
+
+
+def run_gpu(args, w):
+    import torch
+
+    from quantized_paged_kv_akv_amd import binding as B
+    from quantized_paged_kv_akv_amd import configs
+
+    device = torch.device("cuda", 0)
+    torch.cuda.set_device(device)
+    log(f"[bench] building {w.name}: {w.layers} layers, lengths {w.lengths[:4]}...")
+    t0 = time.time()
+    plan, layers, T, qt_ms, n_quant = build_layers(w, device)
+    log(f"[bench] inputs resident in HBM after {time.time() - t0:.1f}s")
+    Hkv, G, D = w.num_kv_heads, w.group, w.head_dim
+    dims = B.dims(Hkv, G)
+    batch = w.batch
+    rows = batch * w.num_q_heads
+    sigma = configs.SIGMA
+    m8, mw, mf = T["t8"].shape[1], T["tw"].shape[1], T["tf"].shape[1]
+    ws = torch.empty(max(B.akv_decode_workspace_bytes(dims, batch, m) for m in (m8, mw, mf)), dtype=torch.uint8,
+                     device=device)
+    o8 = torch.empty((batch, w.num_q_heads, D), device=device)
+    l8 = torch.empty((batch, w.num_q_heads), device=device)
+    ow = torch.empty_like(o8)
+    lw = torch.empty_like(l8)
+    out = [torch.empty_like(o8) for _ in range(w.layers)]
+    outl = [torch.empty_like(l8) for _ in range(w.layers)]
+    stream = torch.cuda.current_stream()
+
+    wsh = torch.empty(max(16, B.akv_decode_hybrid_workspace_bytes(dims, batch, m8, mw)), dtype=torch.uint8,
+                      device=device)
+
+    def hybrid_step():
+        # one layer = akv_decode_hybrid: split-K kernel over int8 + window pages, then the exact fold
+        for i, L in enumerate(layers):
+            B.akv_decode_hybrid(dims, batch, L["q"], L["k_codes"], L["v_codes"], L["k_chan"], L["k_tok"],
+                                L["v_chan"], T["t8"], T["n8"], m8, L["k_pool"], L["v_pool"], T["tw"], T["nw"], mw,
+                                sigma, out[i], outl[i], wsh, stream)
+
+    def four_call_step():
+        # the same layer as the four separate entry points (int8, exact, merge)
+        for i, L in enumerate(layers):
+            B.akv_decode_attn_int8(dims, batch, L["q"], L["k_codes"], L["v_codes"], L["k_chan"], L["k_tok"],
+                                   L["v_chan"], T["t8"], T["n8"], m8, sigma, out[i], outl[i], ws, stream)
+            B.akv_decode_attn_exact(dims, batch, L["q"], L["k_pool"], L["v_pool"], T["tw"], T["nw"], mw, sigma,
+                                    ow, lw, ws, stream)
+            B.akv_merge_lse(rows, D, out[i], outl[i], ow, lw, stream)
+
+    def bf16_step():
+        for i, L in enumerate(layers):
+            B.akv_decode_attn_exact(dims, batch, L["q"], L["k_pool"], L["v_pool"], T["tf"], T["nf"], mf, sigma,
+                                    out[i], outl[i], ws, stream)
+
+    def timed(fn, steps, warmup):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    def split_kernel_us(fn, steps):
+        """Average duration of the split-K kernel of each decode call, from HIP
+        events the library records around that kernel on `stream`."""
+        evs = []
+        for _ in range(steps):
+            for i in range(w.layers):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                b.record(stream)
+                evs.append((a, b))
+        torch.cuda.synchronize()
+        it = iter(evs)
+        orig = B.akv_decode_hybrid if fn is hybrid_step else B.akv_decode_attn_exact
+
+        def hooked(*args, **kw):
+            a, b = next(it)
+            B.akv_set_profile_events(a, b)
+            try:
+                orig(*args, **kw)
+            finally:
+                B.akv_set_profile_events(None, None)
+        name = "akv_decode_hybrid" if fn is hybrid_step else "akv_decode_attn_exact"
+        setattr(B, name, hooked)
+        try:
+            for _ in range(steps):
+                fn()
+        finally:
+            setattr(B, name, orig)
+        torch.cuda.synchronize()
+        d = [a.elapsed_time(b) * 1e3 for a, b in evs]
+        return sum(d) / len(d)
+
+    log("[bench] hybrid step (fused entry) warmup + timed")
+    ms_hybrid = timed(hybrid_step, args.steps, args.warmup)
+    hyb_us = split_kernel_us(hybrid_step, max(2, args.steps // 2))
+    log("[bench] four-call step")
+    ms_four = timed(four_call_step, max(2, args.steps // 2), 1)
+    log("[bench] all-BF16 step")
+    ms_bf16 = timed(bf16_step, max(2, args.steps // 2), 1)
+    bf16_us = split_kernel_us(bf16_step, 2)
+
+    by = step_kv_bytes(plan, Hkv)
+    layer_bytes = by["int8"] + by["window"]
+    hybrid_bytes = layer_bytes * w.layers
+    bf16_bytes = by["bf16_all"] * w.layers
+    quant_ms = sum(qt_ms[1:]) / max(1, len(qt_ms) - 1) if len(qt_ms) > 1 else qt_ms[0]
+    quant_bytes = n_quant * Hkv * (PAGE_BF16_BYTES + PAGE_INT8_BYTES)
+    return dict(ms_hybrid=ms_hybrid, ms_four=ms_four, ms_bf16=ms_bf16, hybrid_bytes=hybrid_bytes,
+                bf16_bytes=bf16_bytes, hyb_launch_us=hyb_us, hyb_bytes_per_launch=layer_bytes,
+                hyb_achieved_gbps=layer_bytes / (hyb_us * 1e-6) / 1e9,
+                bf16_launch_us=bf16_us, bf16_achieved_gbps=by["bf16_all"] / (bf16_us * 1e-6) / 1e9,
+                quant_ms_per_layer=quant_ms, quant_gbps=quant_bytes / (quant_ms * 1e-3) / 1e9)
+
+
+def cpu_baseline(w):
+    """The float64 oracle, as it stands, on a bounded sample of the workload:
+    64 independent (request, KV head) units at this context length -- as many
+    units as one 16-layer step of 4 KV heads -- all reading one KV head's
+    pages (int8-path formula over the old pages, exact window, LSE merge).
+    Scaled to µs per full decode step."""
+    import numpy as np
+
+    from oracle import oracle as O
+    from quantized_paged_kv_akv_amd import configs, inputs
+
+    units = 64
+    w1 = inputs.Workload(w.name + "-1head", w.cfg_id, batch=1, layers=1, num_kv_heads=1, group=w.group,
+                         lengths=w.lengths[:1], window=w.window, outlier_frac=w.outlier_frac, permute=False)
+    t0 = time.time()
+    d = inputs.make_layer_np(w1, 0)
+    plan = d["plan"]
+    src, dst = plan.quant_src_dst()
+    qz = O.quantize_pages(d["k_pool"], d["v_pool"], src, dst, plan.int8_slots_total, 1)
+    log(f"[bench] cpu baseline sample prepared in {time.time() - t0:.1f}s")
+    q = np.repeat(d["q"], units, axis=0)
+    t8 = np.repeat(plan.int8_table(), units, axis=0)
+    tw = np.repeat(plan.window_table(), units, axis=0)
+    n8 = np.full(units, plan.n8[0], np.int32)
+    nw = np.full(units, plan.win_tokens[0], np.int32)
+    t0 = time.time()
+    o8, l8 = O.decode_int8(q, qz["k_codes"], qz["v_codes"], qz["k_chan"], qz["k_tok"], qz["v_chan"], t8, n8, 1,
+                           w.group, configs.SIGMA, mode=1)
+    ow, lw = O.decode_exact(q, d["k_pool"], d["v_pool"], tw, nw, 1, w.group, configs.SIGMA)
+    rows = units * w.group
+    O.merge(np.stack([o8.reshape(rows, 256), ow.reshape(rows, 256)]), np.stack([l8.reshape(rows), lw.reshape(rows)]))
+    wall = time.time() - t0
+    per_step_units = w.batch * w.layers * w.num_kv_heads
+    us_per_step = wall * 1e6 * per_step_units / units
+    threads = min(O.num_threads(), units)
+    return dict(value=us_per_step, unit="us/decode step", cores=threads, kind="oracle",
+                sample=f"{units} (request, KV head) units of one {w.name} layer "
+                       f"({plan.n8[0]} int8 pages + {plan.win_tokens[0]}-token window each), "
+                       f"float64, {wall:.1f}s wall, scaled x{per_step_units / units:g} to one 16-layer step",
+                wall_s=wall)
+
+
+def load_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source."""
+    p = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        t = json.load(open(p))
+    except Exception:
+        return None
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="ctx128k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only (the path is measured on one GPU's share; "
+              "sharding across GPUs is described in DESIGN.md, not built). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    from quantized_paged_kv_akv_amd import configs
+    w = configs.ALL[args.workload]()
+    r = run_gpu(args, w)
+    ms = r["ms_hybrid"]
+    value = r["hybrid_bytes"] / (ms * 1e-3) / 1e9
+    res = {
+        "metric": "\u00b5s/decode step + KV bytes/s (% of HBM peak) at 128K, int8 hybrid vs BF16",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic (seeded on-device draws: K ~ N(0,1)*logU[0.1,10] per channel, V ~ N(0,1)*logU[0.5,2], "
+                "2% outlier tokens x8; pages quantized by akv_quantize_pages)",
+        "config": {"workload": w.name, "context_tokens": int(w.lengths[0]), "batch": w.batch,
+                   "layers": w.layers, "kv_heads": w.num_kv_heads, "group": w.group, "head_dim": w.head_dim,
+                   "page": w.page, "bf16_window_tokens": w.window, "parallelism": "single GPU",
+                   "launch": "eager; per layer akv_decode_hybrid = split-K kernel + combine kernel"},
+        "roofline": {"bound": "hbm", "achieved": round(r["hyb_achieved_gbps"], 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(r["hyb_achieved_gbps"] / HBM_PEAK_GBPS, 4),
+                     "traffic": load_traffic("decode_hybrid_kernel", w.name),
+                     "kernel": "decode_hybrid_kernel (int8 pages + BF16 window of one layer)",
+                     "bytes_per_launch": r["hyb_bytes_per_launch"],
+                     "avg_launch_us": round(r["hyb_launch_us"], 3)},
+        "extra": {
+            "us_per_step_hybrid": round(ms * 1e3, 2),
+            "us_per_layer_hybrid": round(ms * 1e3 / w.layers, 2),
+            "hybrid_kv_bytes_per_step": r["hybrid_bytes"],
+            "hybrid_frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
+            "us_per_step_four_call": round(r["ms_four"] * 1e3, 2),
+            "us_per_step_bf16_all": round(r["ms_bf16"] * 1e3, 2),
+            "bf16_split_kernel_us": round(r["bf16_launch_us"], 2),
+            "bf16_split_kernel_GBps": round(r["bf16_achieved_gbps"], 1),
+            "bf16_kv_bytes_per_step": r["bf16_bytes"],
+            "bf16_GBps": round(r["bf16_bytes"] / (r["ms_bf16"] * 1e-3) / 1e9, 1),
+            "hybrid_speedup_vs_bf16": round(r["ms_bf16"] / ms, 3),
+            "quantize_ms_per_layer": round(r["quant_ms_per_layer"], 3),
+            "quantize_GBps_read_plus_write": round(r["quant_gbps"], 1),
+        },
+    }
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(w)
+        res["cpu_baseline"] = {k: (round(v, 1) if isinstance(v, float) else v) for k, v in cb.items()}
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

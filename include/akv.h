@@ -1,0 +1,255 @@
+/*
+ * akv.h -- C ABI of libakv.so: ActiveKV hybrid-tier decode attention on
+ * AMD MI355X (gfx950).
+ *
+ * The pages this follows (cited by page title and section):
+ *   "Model quantization" page, "An 8-bit page format shaped for its kernel"
+ *       -- the 8-bit page format and when pages are converted.
+ *   "SYCL" page, "Attention that reads 8-bit history"
+ *       -- decode that reads the int8 pages directly.
+ *   "SYCL" page, "Exact tricks and a two-owner decoder"
+ *       -- two requests with equal page counts served by one launch.
+ *   "SYCL" page, "A merge that joins the tiers"
+ *       -- log-sum-exp output starting at -inf; merge into one FP32
+ *          accumulator.
+ *   "ActiveKV" page, "The idea" and "What I built"
+ *       -- exact BF16 tier, hybrid tier, host-authoritative pinned history,
+ *          budgeted staging with a fence-safe lifecycle, explicit refusal.
+ *
+ * Conventions for every call:
+ *   - Tensor pointers are DEVICE pointers unless stated otherwise.  The
+ *     caller owns every buffer, including workspaces and ring slots; the
+ *     library allocates no device memory and never synchronizes the host.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the
+ *     default stream).  The return value reports host-side argument checks
+ *     and launch errors only; device faults surface at the caller's sync.
+ *   - Pointers to tensors must be 16-byte aligned (AKV_ERR_ALIGN otherwise).
+ *   - No C++ exception crosses this interface.  akv_last_error() gives a
+ *     thread-local message for the last failing call.
+ *
+ * Shapes: Hkv KV heads, G query heads per KV head (Hq = Hkv*G; query head j
+ * reads KV head j / G), head dimension D, page size P tokens.  Supported:
+ * D = 256, P = 64, 1 <= G <= 8, Hkv >= 1 (AKV_ERR_UNSUPPORTED otherwise).
+ *
+ * Layouts (row-major, innermost last):
+ *   q        BF16 [B][Hq][D]
+ *   BF16 pool  K  [slot][Hkv][P][D]   token-major
+ *              V  [slot][Hkv][D][P]   channel-major (a page of values is
+ *                                     stored transposed, so each channel's
+ *                                     64 tokens are contiguous)
+ *   int8 pool  k_codes [slot][Hkv][P][D]   int8, token-major
+ *              v_codes [slot][Hkv][D][P]   int8, channel-major
+ *              k_chan  [slot][Hkv][D]      FP32 per-channel key factor
+ *              k_tok   [slot][Hkv][P]      FP32 per-token key factor
+ *              v_chan  [slot][Hkv][D]      FP32 per-channel value scale
+ *   page tables int32 [B][max_pages]  (pool slot of each page, in order)
+ *   outputs  O FP32 [B][Hq][D] (normalised), LSE FP32 [B][Hq]
+ *
+ * LSE is the natural log of sum_t exp(softmax_scale * q . k_t).  A request
+ * with no tokens yields O = 0 and LSE = -inf (a valid empty partial).
+ */
+#ifndef AKV_H
+#define AKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    AKV_OK = 0,
+    AKV_ERR_ARG = -1,         /* null pointer, negative size, bad shape   */
+    AKV_ERR_UNSUPPORTED = -2, /* D != 256, P != 64, G outside [1, 8]      */
+    AKV_ERR_ALIGN = -3,       /* tensor pointer not 16-byte aligned       */
+    AKV_ERR_WORKSPACE = -4,   /* workspace smaller than the query result  */
+    AKV_ERR_BUDGET = -5,      /* staging request exceeds the ring's slot  */
+    AKV_ERR_HIP = -6,         /* a HIP runtime call failed                */
+    AKV_ERR_STATE = -7        /* ring used out of its lifecycle order     */
+} akv_status;
+
+typedef struct {
+    int32_t num_kv_heads; /* Hkv                                  */
+    int32_t group;        /* G query heads per KV head            */
+    int32_t head_dim;     /* D, must be 256                       */
+    int32_t page_size;    /* P, must be 64                        */
+} akv_dims;
+
+/* Human-readable name of a status code (static string). */
+const char *akv_status_string(akv_status s);
+/* Message describing the last failure on the calling thread ("" if none). */
+const char *akv_last_error(void);
+/* Library version, e.g. "akv 0.1.0 gfx950". */
+const char *akv_version(void);
+
+/*
+ * Instrumentation (the "ActiveKV" page, "What I built", keeps instrumented
+ * runs apart from product timing): on the calling thread, record start_event
+ * right before and stop_event right after the split-K kernel of each
+ * subsequent decode call (int8, exact or hybrid), on that call's stream.
+ * Both hipEvent_t handles are owned by the caller; pass NULL, NULL to stop.
+ * Errors: AKV_ERR_ARG if exactly one of them is NULL.
+ */
+akv_status akv_set_profile_events(void *start_event, void *stop_event);
+
+/*
+ * akv_quantize_pages -- convert n full BF16 pages into the 8-bit page format.
+ * ("Model quantization" page, "An 8-bit page format shaped for its kernel".)
+ *
+ * For each i < n and each KV head h, reads BF16 page src_slot[i] of
+ * (k_bf16, v_bf16) and writes int8 page dst_slot[i] of the int8 pool:
+ *   key channel factor  c_d = clamp(sqrt(RMS_d) / g, 2^-14, 2^14), where
+ *       RMS_d is over the page's 64 tokens and g is the geometric mean of
+ *       sqrt(RMS) over channels with nonzero RMS (zero channels: c_d = 1);
+ *   key token factor    s_t = max_d(|K[t][d]| / c_d) / 127;
+ *   value scale         vs_d = max_t |V[t][d]| / 127;
+ *   codes               round-half-even(K / (c_d s_t)), round-half-even(V / vs_d),
+ *                       clamped to [-127, 127]; a zero scale gives code 0.
+ * Scale arithmetic is float64, stored FP32 (round to nearest); the code
+ * quotient is an IEEE float64 divide of the FP32 scales' exact product.
+ * Only full pages are accepted: a page still being written is served by the
+ * exact tier until it is converted.
+ *
+ * src_slot, dst_slot: int32 [n] device arrays.  n = 0 is a no-op.
+ * Errors: AKV_ERR_ARG (null pointer, n < 0), AKV_ERR_UNSUPPORTED, AKV_ERR_ALIGN.
+ */
+akv_status akv_quantize_pages(const akv_dims *dims, int32_t n,
+                              const uint16_t *k_bf16, const uint16_t *v_bf16,
+                              const int32_t *src_slot, const int32_t *dst_slot,
+                              int8_t *k_codes, int8_t *v_codes,
+                              float *k_chan, float *k_tok, float *v_chan,
+                              void *stream);
+
+/*
+ * Workspace (bytes, device memory) that akv_decode_attn_int8 and
+ * akv_decode_attn_exact need for `batch` requests with page tables of
+ * `max_pages` columns: split-K partial outputs.  Deterministic in its
+ * arguments; 0 for empty problems.
+ */
+size_t akv_decode_workspace_bytes(const akv_dims *dims, int32_t batch, int32_t max_pages);
+
+/*
+ * akv_decode_attn_int8 -- single-query paged decode that reads int8 pages
+ * without expanding them.  ("SYCL" page, "Attention that reads 8-bit
+ * history"; "Exact tricks and a two-owner decoder".)
+ *
+ * For request b and query head j, attends q[b][j] over the n_pages[b] int8
+ * pages page_table[b][0 .. n_pages[b]) of KV head j / G:
+ *   z_t = softmax_scale * s_t * sum_d (q_d c_d) code_td   (channel factor
+ *         folded into the query, token factor after the dot);
+ *   online softmax over pages; P times the raw value codes per page, scaled
+ *   by the page's per-channel value scale at the page boundary.
+ * Writes the normalised out_o[b][j][:] and out_lse[b][j] (natural log).
+ * n_pages[b] = 0 gives O = 0, LSE = -inf.  Any batch size works; batch = 2
+ * with equal page counts is the two-owner launch (each request has its own
+ * page-table row and its own output rows).
+ *
+ * n_pages: int32 [batch] device array, each in [0, max_pages].
+ * workspace: at least akv_decode_workspace_bytes(dims, batch, max_pages).
+ * Errors: AKV_ERR_ARG, AKV_ERR_UNSUPPORTED, AKV_ERR_ALIGN, AKV_ERR_WORKSPACE.
+ */
+akv_status akv_decode_attn_int8(const akv_dims *dims, int32_t batch, const uint16_t *q,
+                                const int8_t *k_codes, const int8_t *v_codes,
+                                const float *k_chan, const float *k_tok, const float *v_chan,
+                                const int32_t *page_table, const int32_t *n_pages,
+                                int32_t max_pages, float softmax_scale,
+                                float *out_o, float *out_lse,
+                                void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * akv_decode_attn_exact -- exact BF16 paged decode that also returns the
+ * log-sum-exp statistic.  ("SYCL" page, "A merge that joins the tiers":
+ * the paged decode gains an LSE output initialised to -inf.)
+ *
+ * For request b, attends over the first seq_len[b] tokens of the BF16 pages
+ * page_table[b][0 .. ceil(seq_len[b] / P)); the last page may be partial
+ * (tokens past seq_len are masked).  seq_len[b] = 0 gives O = 0, LSE = -inf.
+ * seq_len: int32 [batch] device array, each in [0, max_pages * P].
+ * Errors as akv_decode_attn_int8.
+ */
+akv_status akv_decode_attn_exact(const akv_dims *dims, int32_t batch, const uint16_t *q,
+                                 const uint16_t *k_bf16, const uint16_t *v_bf16,
+                                 const int32_t *page_table, const int32_t *seq_len,
+                                 int32_t max_pages, float softmax_scale,
+                                 float *out_o, float *out_lse,
+                                 void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * akv_decode_hybrid -- one layer of the hybrid tier in two launches: the
+ * int8 pages (as akv_decode_attn_int8) and the BF16 recent window (as
+ * akv_decode_attn_exact) are decoded by one split-K launch whose partials
+ * all fold, exactly, in one second pass.  ("ActiveKV" page, "The idea":
+ * recent context exact, older history 8-bit, combined with exact attention
+ * arithmetic; "SYCL" page, "A merge that joins the tiers".)
+ *
+ * The result equals akv_merge_lse of the two separate calls' outputs up to
+ * FP32 rounding order.  Either tier may be empty (max_pages_* = 0 or zero
+ * counts); both empty gives O = 0, LSE = -inf.
+ * workspace: at least akv_decode_hybrid_workspace_bytes(dims, batch,
+ * max_pages_int8, max_pages_window).
+ * Errors: AKV_ERR_ARG, AKV_ERR_UNSUPPORTED, AKV_ERR_ALIGN, AKV_ERR_WORKSPACE.
+ */
+size_t akv_decode_hybrid_workspace_bytes(const akv_dims *dims, int32_t batch, int32_t max_pages_int8,
+                                         int32_t max_pages_window);
+akv_status akv_decode_hybrid(const akv_dims *dims, int32_t batch, const uint16_t *q,
+                             const int8_t *k_codes, const int8_t *v_codes,
+                             const float *k_chan, const float *k_tok, const float *v_chan,
+                             const int32_t *page_table_int8, const int32_t *n_pages_int8,
+                             int32_t max_pages_int8,
+                             const uint16_t *k_bf16, const uint16_t *v_bf16,
+                             const int32_t *page_table_window, const int32_t *window_len,
+                             int32_t max_pages_window, float softmax_scale,
+                             float *out_o, float *out_lse,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * akv_merge_lse -- fold one partial into an FP32 accumulator, exactly.
+ * ("SYCL" page, "A merge that joins the tiers".)
+ *
+ * For each of `rows` rows:  L = log(exp(acc_lse) + exp(part_lse));
+ *   acc_o = exp(acc_lse - L) acc_o + exp(part_lse - L) part_o;  acc_lse = L.
+ * A -inf LSE is an empty partial: merging it leaves the other side as is;
+ * two empties give O = 0, LSE = -inf.  acc_o/acc_lse are read and written
+ * in place (start them with akv_fill_empty).  acc_o, part_o: [rows][head_dim].
+ * Errors: AKV_ERR_ARG, AKV_ERR_ALIGN.
+ */
+akv_status akv_merge_lse(int32_t rows, int32_t head_dim, float *acc_o, float *acc_lse,
+                         const float *part_o, const float *part_lse, void *stream);
+
+/* Set rows to the empty partial: O = 0, LSE = -inf (a kernel, graph-safe). */
+akv_status akv_fill_empty(int32_t rows, int32_t head_dim, float *o, float *lse, void *stream);
+
+/*
+ * Host-staged mode ("ActiveKV" page, "The idea" and "What I built"): the
+ * authoritative history sits in pinned host memory and each step stages one
+ * layer at a time into a ring of device slots, with events so a slot is
+ * never overwritten while a copy or kernel still uses it.
+ *
+ * akv_ring_create: slots[i] are caller-owned device buffers of slot_bytes
+ *   each (n_slots >= 2).  The ring owns only its HIP events.
+ * akv_ring_stage: for `layer`, waits (on copy_stream) until the slot
+ *   layer % n_slots was released by its previous user, enqueues n_srcs
+ *   host-to-device copies (host_srcs[k] must be pinned host memory) packed
+ *   back to back at 256-byte aligned offsets into that slot, records
+ *   copy-done, and makes compute_stream wait for it.  *slot_out receives
+ *   the slot's device address and offsets[k] (if not NULL) each source's
+ *   offset.  A request larger than slot_bytes returns AKV_ERR_BUDGET before
+ *   anything is enqueued.  Staging a layer whose slot has not been released
+ *   since it was last staged returns AKV_ERR_STATE.
+ * akv_ring_release: records on compute_stream that `layer`'s slot may be
+ *   reused (call after the kernels that read it are enqueued).
+ * akv_ring_destroy: releases the events (synchronizes them first).
+ */
+typedef struct akv_ring akv_ring;
+akv_status akv_ring_create(void *const *slots, size_t slot_bytes, int32_t n_slots, akv_ring **out);
+akv_status akv_ring_stage(akv_ring *ring, int32_t layer, const void *const *host_srcs,
+                          const size_t *bytes, int32_t n_srcs, void *copy_stream,
+                          void *compute_stream, void **slot_out, size_t *offsets);
+akv_status akv_ring_release(akv_ring *ring, int32_t layer, void *compute_stream);
+akv_status akv_ring_destroy(akv_ring *ring);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* AKV_H */

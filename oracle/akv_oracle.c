@@ -194,14 +194,16 @@ static void akvo_load_bf16_page(int Hkv, int D, int P, const uint16_t *kpool,
 /* dst[i], all KV heads.  Writes codes in the pool layouts and FP32 scales.  */
 /* If use_given_scales != 0 the scales already in k_chan/k_tok/v_chan are    */
 /* used for stage 2 (stage-2 agreement check) and left unchanged.            */
-/* tie_count receives the number of exact ties.  [FMT]                       */
+/* tie_count receives the number of exact ties; k_ties / v_ties (may be      */
+/* NULL) receive 0/1 tie masks in the code pools' layouts.  [FMT]            */
 /* ------------------------------------------------------------------------- */
 int akvo_quantize_pages(int n, int Hkv, int D, int P,
                         const uint16_t *kpool, const uint16_t *vpool,
                         const int32_t *src, const int32_t *dst,
                         int8_t *kcodes, int8_t *vcodes,
                         float *k_chan, float *k_tok, float *v_chan,
-                        int use_given_scales, int64_t *tie_count)
+                        int use_given_scales, int64_t *tie_count,
+                        uint8_t *k_ties, uint8_t *v_ties)
 {
     int64_t ties_total = 0;
     int err = 0;
@@ -214,7 +216,9 @@ int akvo_quantize_pages(int n, int Hkv, int D, int P,
         double *c64 = (double *)malloc(sizeof(double) * (size_t)D);
         int8_t *kc = (int8_t *)malloc(PD);
         int8_t *vc = (int8_t *)malloc(PD);
-        if (!K || !V || !c64 || !kc || !vc) {
+        uint8_t *kt = (uint8_t *)malloc(PD);
+        uint8_t *vt = (uint8_t *)malloc(PD);
+        if (!K || !V || !c64 || !kc || !vc || !kt || !vt) {
             err |= 1;
         } else {
             akvo_load_bf16_page(Hkv, D, P, kpool, vpool, src[i], h, K, V);
@@ -223,16 +227,18 @@ int akvo_quantize_pages(int n, int Hkv, int D, int P,
             float *s32 = k_tok + ph * P;
             float *vs32 = v_chan + ph * D;
             if (!use_given_scales) akvo_page_scales(P, D, K, V, c64, c32, s32, vs32);
-            ties_total += akvo_page_codes(P, D, K, V, c32, s32, vs32, kc, vc, NULL, NULL);
+            ties_total += akvo_page_codes(P, D, K, V, c32, s32, vs32, kc, vc, kt, vt);
             int8_t *kout = kcodes + ph * PD;
             int8_t *vout = vcodes + ph * PD;
             for (int t = 0; t < P; ++t)
                 for (int d = 0; d < D; ++d) {
                     kout[(size_t)t * D + d] = kc[(size_t)t * D + d];
                     vout[(size_t)d * P + t] = vc[(size_t)t * D + d];
+                    if (k_ties) k_ties[ph * PD + (size_t)t * D + d] = kt[(size_t)t * D + d];
+                    if (v_ties) v_ties[ph * PD + (size_t)d * P + t] = vt[(size_t)t * D + d];
                 }
         }
-        free(K); free(V); free(c64); free(kc); free(vc);
+        free(K); free(V); free(c64); free(kc); free(vc); free(kt); free(vt);
     }
     if (tie_count) *tie_count = ties_total;
     return err ? -2 : 0;

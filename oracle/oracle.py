@@ -59,7 +59,7 @@ def _load():
         D = ctypes.c_double
         _lib.akvo_page_scales.argtypes = [I, I, P, P, P, P, P, P]
         _lib.akvo_page_codes.argtypes = [I, I, P, P, P, P, P, P, P, P, P]
-        _lib.akvo_quantize_pages.argtypes = [I, I, I, I, P, P, P, P, P, P, P, P, P, I, P]
+        _lib.akvo_quantize_pages.argtypes = [I, I, I, I, P, P, P, P, P, P, P, P, P, I, P, P, P]
         _lib.akvo_attend.argtypes = [I, I, P, P, P, D, P, P]
         _lib.akvo_merge.argtypes = [I, I, I, P, P, P, P]
         _lib.akvo_decode_exact.argtypes = [I, I, I, I, I, P, P, P, P, P, I, D, P, P]
@@ -130,7 +130,8 @@ def quantize_pages(kpool, vpool, src, dst, n_slots_out, Hkv, D=256, P=64, given=
 
     kpool uint16 [slots][Hkv][P][D], vpool uint16 [slots][Hkv][D][P].
     ``given`` = (k_chan, k_tok, v_chan) to run stage 2 only with those scales.
-    Returns dict(k_codes, v_codes, k_chan, k_tok, v_chan, ties)."""
+    Returns dict(k_codes, v_codes, k_chan, k_tok, v_chan, ties, k_ties, v_ties);
+    the tie masks mark codes whose float64 quotient was exactly k + 0.5."""
     kpool = _c(kpool, np.uint16)
     vpool = _c(vpool, np.uint16)
     src = _c(src, np.int32)
@@ -147,12 +148,14 @@ def quantize_pages(kpool, vpool, src, dst, n_slots_out, Hkv, D=256, P=64, given=
         k_chan, k_tok, v_chan = (_c(a, np.float32).copy() for a in given)
         use = 1
     ties = np.zeros(1, np.int64)
+    kt = np.zeros(kc.shape, np.uint8)
+    vt = np.zeros(vc.shape, np.uint8)
     rc = _load().akvo_quantize_pages(n, Hkv, D, P, _p(kpool), _p(vpool), _p(src), _p(dst),
                                      _p(kc), _p(vc), _p(k_chan), _p(k_tok), _p(v_chan), use,
-                                     _p(ties))
+                                     _p(ties), _p(kt), _p(vt))
     assert rc == 0, rc
     return dict(k_codes=kc, v_codes=vc, k_chan=k_chan, k_tok=k_tok, v_chan=v_chan,
-                ties=int(ties[0]))
+                ties=int(ties[0]), k_ties=kt.astype(bool), v_ties=vt.astype(bool))
 
 
 # --------------------------------------------------------------------------- attention

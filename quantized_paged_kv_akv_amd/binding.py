@@ -1,0 +1,248 @@
+"""ctypes binding of libakv.so -- argument marshalling only.
+
+Each function has the name of the C entry point it calls (include/akv.h) and
+takes torch tensors for the device buffers: it checks device, dtype and
+contiguity, passes raw pointers and the current HIP stream, and raises
+``AkvError`` on a non-OK status.  All computation happens in the library's
+HIP kernels; there is no fallback.  Importing this module raises if the
+library has not been built (``python -m quantized_paged_kv_akv_amd.build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libakv.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "akv.h")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -m quantized_paged_kv_akv_amd.build`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_sz = ctypes.c_size_t
+_f32 = ctypes.c_float
+
+
+class akv_dims(ctypes.Structure):
+    _fields_ = [("num_kv_heads", _i32), ("group", _i32), ("head_dim", _i32), ("page_size", _i32)]
+
+
+def dims(num_kv_heads: int, group: int, head_dim: int = 256, page_size: int = 64) -> akv_dims:
+    return akv_dims(num_kv_heads, group, head_dim, page_size)
+
+
+_D = ctypes.POINTER(akv_dims)
+
+_SIGS = {
+    "akv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "akv_last_error": (ctypes.c_char_p, []),
+    "akv_version": (ctypes.c_char_p, []),
+    "akv_set_profile_events": (ctypes.c_int, [_vp, _vp]),
+    "akv_quantize_pages": (ctypes.c_int, [_D, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "akv_decode_workspace_bytes": (_sz, [_D, _i32, _i32]),
+    "akv_decode_attn_int8": (ctypes.c_int, [_D, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _f32,
+                                            _vp, _vp, _vp, _sz, _vp]),
+    "akv_decode_attn_exact": (ctypes.c_int, [_D, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _f32, _vp, _vp, _vp,
+                                             _sz, _vp]),
+    "akv_decode_hybrid_workspace_bytes": (_sz, [_D, _i32, _i32, _i32]),
+    "akv_decode_hybrid": (ctypes.c_int, [_D, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp,
+                                         _vp, _i32, _f32, _vp, _vp, _vp, _sz, _vp]),
+    "akv_merge_lse": (ctypes.c_int, [_i32, _i32, _vp, _vp, _vp, _vp, _vp]),
+    "akv_fill_empty": (ctypes.c_int, [_i32, _i32, _vp, _vp, _vp]),
+    "akv_ring_create": (ctypes.c_int, [ctypes.POINTER(_vp), _sz, _i32, ctypes.POINTER(_vp)]),
+    "akv_ring_stage": (ctypes.c_int, [_vp, _i32, ctypes.POINTER(_vp), ctypes.POINTER(_sz), _i32, _vp, _vp,
+                                      ctypes.POINTER(_vp), ctypes.POINTER(_sz)]),
+    "akv_ring_release": (ctypes.c_int, [_vp, _i32, _vp]),
+    "akv_ring_destroy": (ctypes.c_int, [_vp]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+STATUS = {0: "AKV_OK", -1: "AKV_ERR_ARG", -2: "AKV_ERR_UNSUPPORTED", -3: "AKV_ERR_ALIGN",
+          -4: "AKV_ERR_WORKSPACE", -5: "AKV_ERR_BUDGET", -6: "AKV_ERR_HIP", -7: "AKV_ERR_STATE"}
+
+
+class AkvError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        self.status_name = STATUS.get(status, str(status))
+        super().__init__(f"{fn}: {self.status_name}: {_lib.akv_last_error().decode()}")
+
+
+def header_functions() -> list:
+    """Names of the functions include/akv.h declares."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(akv_[a-z0-9_]+)\s*\(", text)) - {"akv_ring"})
+
+
+def _check(fn: str, st: int):
+    if st != 0:
+        raise AkvError(fn, st)
+
+
+def _stream(stream) -> _vp:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return _vp(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _ptr(t: Optional[torch.Tensor], dtypes, name: str) -> _vp:
+    if t is None:
+        return _vp(0)
+    if not isinstance(dtypes, (tuple, list)):
+        dtypes = (dtypes,)
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: expected a device tensor, got {t.device}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name}: expected dtype {dtypes}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous tensor")
+    return _vp(t.data_ptr())
+
+
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def version() -> str:
+    return _lib.akv_version().decode()
+
+
+def akv_set_profile_events(start_event=None, stop_event=None):
+    """torch.cuda.Event pair (already recorded once, so the HIP event exists) or None."""
+    a = _vp(start_event.cuda_event) if start_event is not None else _vp(0)
+    b = _vp(stop_event.cuda_event) if stop_event is not None else _vp(0)
+    _check("akv_set_profile_events", _lib.akv_set_profile_events(a, b))
+
+
+def akv_quantize_pages(d: akv_dims, n: int, k_bf16, v_bf16, src_slot, dst_slot, k_codes, v_codes, k_chan,
+                       k_tok, v_chan, stream=None):
+    _check("akv_quantize_pages", _lib.akv_quantize_pages(
+        ctypes.byref(d), n, _ptr(k_bf16, _BF16, "k_bf16"), _ptr(v_bf16, _BF16, "v_bf16"),
+        _ptr(src_slot, torch.int32, "src_slot"), _ptr(dst_slot, torch.int32, "dst_slot"),
+        _ptr(k_codes, torch.int8, "k_codes"), _ptr(v_codes, torch.int8, "v_codes"),
+        _ptr(k_chan, torch.float32, "k_chan"), _ptr(k_tok, torch.float32, "k_tok"),
+        _ptr(v_chan, torch.float32, "v_chan"), _stream(stream)))
+
+
+def akv_decode_workspace_bytes(d: akv_dims, batch: int, max_pages: int) -> int:
+    return int(_lib.akv_decode_workspace_bytes(ctypes.byref(d), batch, max_pages))
+
+
+def akv_decode_attn_int8(d: akv_dims, batch: int, q, k_codes, v_codes, k_chan, k_tok, v_chan, page_table,
+                         n_pages, max_pages: int, softmax_scale: float, out_o, out_lse, workspace,
+                         stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("akv_decode_attn_int8", _lib.akv_decode_attn_int8(
+        ctypes.byref(d), batch, _ptr(q, _BF16, "q"), _ptr(k_codes, torch.int8, "k_codes"),
+        _ptr(v_codes, torch.int8, "v_codes"), _ptr(k_chan, torch.float32, "k_chan"),
+        _ptr(k_tok, torch.float32, "k_tok"), _ptr(v_chan, torch.float32, "v_chan"),
+        _ptr(page_table, torch.int32, "page_table"), _ptr(n_pages, torch.int32, "n_pages"), max_pages,
+        softmax_scale, _ptr(out_o, torch.float32, "out_o"), _ptr(out_lse, torch.float32, "out_lse"),
+        _ptr(workspace, (torch.uint8, torch.int8, torch.float32), "workspace"), ws_bytes, _stream(stream)))
+
+
+def akv_decode_attn_exact(d: akv_dims, batch: int, q, k_bf16, v_bf16, page_table, seq_len, max_pages: int,
+                          softmax_scale: float, out_o, out_lse, workspace, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("akv_decode_attn_exact", _lib.akv_decode_attn_exact(
+        ctypes.byref(d), batch, _ptr(q, _BF16, "q"), _ptr(k_bf16, _BF16, "k_bf16"),
+        _ptr(v_bf16, _BF16, "v_bf16"), _ptr(page_table, torch.int32, "page_table"),
+        _ptr(seq_len, torch.int32, "seq_len"), max_pages, softmax_scale,
+        _ptr(out_o, torch.float32, "out_o"), _ptr(out_lse, torch.float32, "out_lse"),
+        _ptr(workspace, (torch.uint8, torch.int8, torch.float32), "workspace"), ws_bytes, _stream(stream)))
+
+
+def akv_decode_hybrid_workspace_bytes(d: akv_dims, batch: int, max_pages_int8: int, max_pages_window: int) -> int:
+    return int(_lib.akv_decode_hybrid_workspace_bytes(ctypes.byref(d), batch, max_pages_int8, max_pages_window))
+
+
+def akv_decode_hybrid(d: akv_dims, batch: int, q, k_codes, v_codes, k_chan, k_tok, v_chan, page_table_int8,
+                      n_pages_int8, max_pages_int8: int, k_bf16, v_bf16, page_table_window, window_len,
+                      max_pages_window: int, softmax_scale: float, out_o, out_lse, workspace, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("akv_decode_hybrid", _lib.akv_decode_hybrid(
+        ctypes.byref(d), batch, _ptr(q, _BF16, "q"), _ptr(k_codes, torch.int8, "k_codes"),
+        _ptr(v_codes, torch.int8, "v_codes"), _ptr(k_chan, torch.float32, "k_chan"),
+        _ptr(k_tok, torch.float32, "k_tok"), _ptr(v_chan, torch.float32, "v_chan"),
+        _ptr(page_table_int8, torch.int32, "page_table_int8"), _ptr(n_pages_int8, torch.int32, "n_pages_int8"),
+        max_pages_int8, _ptr(k_bf16, _BF16, "k_bf16"), _ptr(v_bf16, _BF16, "v_bf16"),
+        _ptr(page_table_window, torch.int32, "page_table_window"), _ptr(window_len, torch.int32, "window_len"),
+        max_pages_window, softmax_scale, _ptr(out_o, torch.float32, "out_o"),
+        _ptr(out_lse, torch.float32, "out_lse"),
+        _ptr(workspace, (torch.uint8, torch.int8, torch.float32), "workspace"), ws_bytes, _stream(stream)))
+
+
+def akv_merge_lse(rows: int, head_dim: int, acc_o, acc_lse, part_o, part_lse, stream=None):
+    _check("akv_merge_lse", _lib.akv_merge_lse(
+        rows, head_dim, _ptr(acc_o, torch.float32, "acc_o"), _ptr(acc_lse, torch.float32, "acc_lse"),
+        _ptr(part_o, torch.float32, "part_o"), _ptr(part_lse, torch.float32, "part_lse"), _stream(stream)))
+
+
+def akv_fill_empty(rows: int, head_dim: int, o, lse, stream=None):
+    _check("akv_fill_empty", _lib.akv_fill_empty(rows, head_dim, _ptr(o, torch.float32, "o"),
+                                                 _ptr(lse, torch.float32, "lse"), _stream(stream)))
+
+
+def akv_ring_create(slots: Sequence[torch.Tensor]):
+    """Returns an opaque ring handle over caller-owned device slots."""
+    arr = (_vp * len(slots))(*[_vp(_ptr(t, (torch.uint8, torch.int8), "slot").value) for t in slots])
+    slot_bytes = min(t.numel() * t.element_size() for t in slots)
+    h = _vp()
+    _check("akv_ring_create", _lib.akv_ring_create(arr, slot_bytes, len(slots), ctypes.byref(h)))
+    return h
+
+
+def akv_ring_stage(ring, layer: int, host_srcs: Sequence[torch.Tensor], copy_stream, compute_stream):
+    """Returns (device address of the slot, byte offset of each source in it)."""
+    for t in host_srcs:
+        if t.device.type != "cpu" or not t.is_pinned() or not t.is_contiguous():
+            raise ValueError("host sources must be contiguous pinned CPU tensors")
+    n = len(host_srcs)
+    srcs = (_vp * n)(*[_vp(t.data_ptr()) for t in host_srcs])
+    nbytes = (_sz * n)(*[t.numel() * t.element_size() for t in host_srcs])
+    offs = (_sz * n)()
+    out = _vp()
+    _check("akv_ring_stage", _lib.akv_ring_stage(ring, layer, srcs, nbytes, n, _stream(copy_stream),
+                                                 _stream(compute_stream), ctypes.byref(out), offs))
+    return int(out.value), list(offs)
+
+
+def akv_ring_release(ring, layer: int, compute_stream):
+    _check("akv_ring_release", _lib.akv_ring_release(ring, layer, _stream(compute_stream)))
+
+
+def akv_ring_destroy(ring):
+    _check("akv_ring_destroy", _lib.akv_ring_destroy(ring))
+
+
+class Ring:
+    """Keeps the slot tensors alive next to an akv_ring handle."""
+
+    def __init__(self, slots: Sequence[torch.Tensor]):
+        self.slots = list(slots)
+        self.slot_bytes = min(t.numel() * t.element_size() for t in self.slots)
+        self._h = akv_ring_create(self.slots)
+
+    def stage(self, layer: int, host_srcs, copy_stream, compute_stream):
+        """Returns (slot tensor, byte offsets)."""
+        addr, offs = akv_ring_stage(self._h, layer, host_srcs, copy_stream, compute_stream)
+        slot = next(t for t in self.slots if t.data_ptr() == addr)
+        return slot, offs
+
+    def release(self, layer: int, compute_stream):
+        akv_ring_release(self._h, layer, compute_stream)
+
+    def destroy(self):
+        if self._h is not None:
+            akv_ring_destroy(self._h)
+            self._h = None

@@ -1,0 +1,57 @@
+// akv_host.h -- host-side helpers shared by the C-ABI entry points.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/akv.h"
+
+namespace akv {
+
+// Record a thread-local message for akv_last_error() and return `s`.
+akv_status fail(akv_status s, const char* fmt, ...);
+void clear_error();
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Instrumentation: when the calling thread set a pair of events with
+// akv_set_profile_events, they are recorded on the launch stream right before
+// and right after the split-K kernel of the next decode calls.
+void prof_begin(hipStream_t s);
+void prof_end(hipStream_t s);
+
+// Shape checks common to every attention/quantize call.
+akv_status check_dims(const akv_dims* d);
+
+// Split-K plan for the paged decode kernels: pages per work-group and the
+// number of splits for page tables of `max_pages` columns.
+struct SplitPlan {
+    int pages_per_split;
+    int n_splits;
+};
+SplitPlan plan_splits(const akv_dims* d, int batch, int max_pages);
+
+// Plan of the int8 tier, whose work-groups are four waves that each own
+// pages_per_split consecutive pages: n_splits = ceil(max_pages / (4 * pps)).
+SplitPlan plan_int8_splits(const akv_dims* d, int batch, int max_pages);
+
+// Workspace bytes for `batch` requests with `n_splits` splits each.
+size_t partial_bytes(const akv_dims* d, int batch, int n_splits);
+
+// Split plan for the recent window of the hybrid call: few pages per split so
+// the window's work-groups spread across the chip next to the int8 ones.
+SplitPlan plan_window_splits(const akv_dims* d, int batch, int max_pages);
+
+inline akv_status launch_status(const char* what) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(AKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return AKV_OK;
+}
+
+// Second pass of split-K: fold the n_splits partials of each of `rows` rows
+// (part_o [rows][n_splits][D], part_lse [rows][n_splits]) into out_o/out_lse.
+akv_status launch_combine(int rows, int D, const float* part_o, const float* part_lse, int n_splits, float* out_o,
+                          float* out_lse, hipStream_t stream);
+
+}  // namespace akv

@@ -1,0 +1,729 @@
+// decode.hip -- single-query paged decode over int8 pages and over BF16
+// pages, split-K across pages with a log-sum-exp second pass.
+//
+// int8 tier ("SYCL" page, "Attention that reads 8-bit history"): the key
+// channel factor is folded into the query per page (q' = q (.) c), the
+// per-token key factor multiplies the finished dot product, the softmax
+// weights multiply the raw value codes, and the per-channel value scale is
+// applied to the page's PV result at the page boundary.
+// Exact tier ("SYCL" page, "A merge that joins the tiers"): BF16 decode that
+// also returns the log-sum-exp, -inf for an empty range.
+//
+// Work decomposition (both kernels).  A work-group of 4 waves owns one
+// (split of pages, KV head, request).  Wave w owns channels [64w, 64w+64):
+//   QK   S^T(tokens x heads) = K Q^T over the wave's channels, 16x16x32
+//        MFMAs with 16 token rows per tile and 4 tiles per page; the four
+//        waves' partial sums meet in LDS once per page (the only barrier).
+//   PV   O^T(channels x heads) = V^T P^T for the wave's 64 channels, with V
+//        read channel-major so a lane's 16-byte load is one MFMA operand.
+// The 16 MFMA columns hold the G query heads twice: columns h and h+8 carry
+// head h, so the FP32 softmax weights P can be fed as a high and a low
+// half-precision part (column h: hi, column h+8: lo) in a single MFMA; the
+// two halves of O are added once at the end.  For the int8 tier the query
+// times channel factor is likewise split hi + lo (two MFMAs into one
+// accumulator), after scaling each column by a power of two so FP16 neither
+// overflows nor loses the small channels.  Int8 codes become FP16 exactly.
+//
+// Token order inside a page: A-operand row i of QK tile t is token
+// 16*(i>>2) + 4t + (i&3).  The MFMA result then gives lane group g the tokens
+// 16g .. 16g+15 across the four tiles, which is exactly the contraction slice
+// group g holds for PV (tokens 16g + 8s + e), so P goes from the QK result to
+// the PV operand without leaving the lane.
+//
+// Softmax runs in base 2 (logits scaled by log2 e); LSE is returned in
+// natural log.  Each split writes a normalised partial (O, LSE) to the
+// workspace; combine_kernel folds them exactly.
+#include <math.h>
+
+#include <type_traits>
+
+#include "akv_device.h"
+#include "akv_host.h"
+
+namespace akv {
+
+struct Int8Args {
+    const uint16_t* q;
+    const int8_t* kc;
+    const int8_t* vc;
+    const float* kchan;
+    const float* ktok;
+    const float* vchan;
+    const int32_t* page_table;
+    const int32_t* n_pages;
+    int max_pages, Hkv, G, pps;
+    int col0, n_cols;  // this tier's first partial column and the partial row stride
+    float scale_log2;
+    float* part_o;
+    float* part_lse;
+};
+
+struct ExactArgs {
+    const uint16_t* q;
+    const uint16_t* kb;
+    const uint16_t* vb;
+    const int32_t* page_table;
+    const int32_t* seq_len;
+    int max_pages, Hkv, G, pps;
+    int col0, n_cols;
+    float scale_log2;
+    float* part_o;
+    float* part_lse;
+};
+
+// LDS of the exact tier's body
+struct ExactSmem {
+    float part[2][4][16][64];  // QK partial logits of the four waves, double-buffered
+};
+
+// QK tile t, A-operand row i  ->  token within the page
+__device__ __forceinline__ int qk_row_token(int t, int i) { return 16 * (i >> 2) + 4 * t + (i & 3); }
+
+// Sum the four waves' partial logits for this lane: tile t, row r is token
+// 16g + 4t + r of the page.
+__device__ __forceinline__ void gather_logits(const float (*part)[16][64], int l, float S[16]) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) S[k] = part[0][k][l] + part[1][k][l] + part[2][k][l] + part[3][k][l];
+}
+
+// Online-softmax step on this lane's 16 base-2 logits (masked = -inf):
+// returns alpha (rescale of previous state) and writes P.
+__device__ __forceinline__ float softmax_step(const float z[16], float& M, float& lsum, float p[16]) {
+    float pm = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) pm = fmaxf(pm, z[k]);
+    pm = group_max(pm);
+    const float Mn = fmaxf(M, pm);
+    const float alpha = exp2f(M - Mn);
+    float ps = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        p[k] = exp2f(z[k] - Mn);
+        ps += p[k];
+    }
+    lsum = lsum * alpha + ps;
+    M = Mn;
+    return alpha;
+}
+
+// As softmax_step, with the running reference rounded up to an integer
+// (base 2): every rescale factor is an exact power of two, and it is exactly
+// 1 whenever the page does not lift the reference past the next integer.
+// ("SYCL" page, "Exact tricks and a two-owner decoder".)
+__device__ __forceinline__ float softmax_step_int(const float z[16], float& M, float& lsum, float p[16]) {
+    float pm = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) pm = fmaxf(pm, z[k]);
+    pm = group_max(pm);
+    const float Mn = fmaxf(M, ceilf(pm));
+    const float alpha = exp2f(M - Mn);
+    float ps = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        p[k] = exp2f(z[k] - Mn);
+        ps += p[k];
+    }
+    lsum = lsum * alpha + ps;
+    M = Mn;
+    return alpha;
+}
+
+// P^T operand element (s, e) is token 16g + 8s + e = QK tile 2s + (e>>2), row e&3.
+__device__ __forceinline__ float p_elem(const float p[16], int s, int e) {
+    return p[(2 * s + (e >> 2)) * 4 + (e & 3)];
+}
+
+// Normalise, add the hi/lo halves and write this split's partial.
+__device__ __forceinline__ void write_partial(f32x4 O[4], float M, float lsum, bool valid, bool hi_lane,
+                                              int w, int g, size_t row, int n_cols, int col,
+                                              float* __restrict__ part_o, float* __restrict__ part_lse) {
+    const float L = group_sum(lsum);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) O[j][r] += __shfl_xor(O[j][r], 8, 64);
+    if (valid && hi_lane) {
+        const float inv = 1.0f / L;
+        float* dst = part_o + (row * n_cols + col) * kD + 64 * w + 4 * g;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) *reinterpret_cast<f32x4*>(dst + 16 * j) = O[j] * inv;
+        if (w == 0 && g == 0) part_lse[row * n_cols + col] = (M + log2f(L)) * kLn2;
+    }
+}
+
+// A split with no pages still owns its partial slot: mark it empty.
+__device__ __forceinline__ void write_empty(int G, int Hkv, int kvh, int b, int n_cols, int col,
+                                            float* __restrict__ part_lse) {
+    const int t = threadIdx.x;
+    if (t < G) part_lse[((size_t)b * Hkv * G + (size_t)kvh * G + t) * n_cols + col] = -INFINITY;
+}
+
+// ---------------------------------------------------------------- int8 tier
+// One wave owns whole pages, so a page needs no barrier and its softmax is
+// computed once.  Per page, lane (n, g) of the wave:
+//   QK   tile t (16 tokens) x channel block s2 (64 channels): the lane's
+//        16-byte load K[16(n>>2) + 4t + (n&3)][64 s2 + 16g .. +16] is the A
+//        operand of two k-steps; the B operand is q' = q (.) c of head n&7 over
+//        the same channels, as an FP16 hi part and lo part (two MFMAs into one
+//        accumulator).  64 MFMAs.
+//   softmax over the lane's 16 logits (tokens 16g .. 16g+15) and the group.
+//   PV   channel tile j: the lane's 16-byte load V^T[16j + n][16g .. +16] is
+//        the A operand of two k-steps, P^T the B operand (column n < 8 the hi
+//        part, n >= 8 the lo part).  32 MFMAs.
+// The query's FP32 rows sit in LDS; each query row is pre-scaled by a power
+// of two so max|q| < 1, which with max_d c_d >= 1 (the factors multiply to
+// one) keeps every q' inside FP16's range.  The next page's codes are loaded
+// into the registers the current page frees as it consumes them; its scales
+// go to the other half of a per-wave LDS double buffer.  The four waves of a
+// work-group take consecutive page ranges of one (request, KV head) and merge
+// once at the end.
+constexpr int kMaxPagesPerWave = 64;
+
+struct Int8Smem {
+    float q[kMaxGroup][kD];        // query rows (scaled by 2^-e per row), FP32
+    float qe[kMaxGroup];           // the row's power-of-two exponent e
+    float sc[4][2][2 * kD + kP];   // per wave, per slot: k_chan | v_chan | k_tok * scale_log2
+    int slot[4][kMaxPagesPerWave]; // pool slots of each wave's pages
+    float mo[4][kMaxGroup][kD];    // end merge: each wave's unnormalised O
+    float mm[4][kMaxGroup];        // ... its running max (base 2)
+    float ml[4][kMaxGroup];        // ... its sum of weights
+};
+
+__device__ __forceinline__ void int8_split(const Int8Args& a, Int8Smem& sm, int split, int kvh, int b) {
+    const int np = min(a.n_pages[b], a.max_pages);
+    const int ppw = a.pps;  // pages per wave
+    const int wg0 = split * 4 * ppw;
+    if (wg0 >= np) {
+        write_empty(a.G, a.Hkv, kvh, b, a.n_cols, a.col0 + split, a.part_lse);
+        return;
+    }
+    const int tid = threadIdx.x, l = tid & 63, n = l & 15, g = l >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+    const int G = a.G, Hkv = a.Hkv, Hq = Hkv * G;
+    const int hh = n & 7;
+    const bool lo_lane = n >= 8;
+    const int pa = min(np, wg0 + w * ppw), pb = min(np, wg0 + (w + 1) * ppw);
+    // per-lane byte offsets inside a page; tile offsets are immediates
+    const uint32_t koff = (uint32_t)(qk_row_token(0, n) * kD + 16 * g);
+    const uint32_t voff = (uint32_t)(n * kP + 16 * g);
+    const int32_t* pt = a.page_table + (size_t)b * a.max_pages;
+    const size_t row0 = (size_t)b * Hq + (size_t)kvh * G;
+
+    // this wave's page slots, read once (the loop reads them from LDS)
+    for (int i = l; i < pb - pa; i += 64) sm.slot[w][i] = pt[pa + i];
+
+    // query rows of this KV head, FP32, each scaled by 2^-e (e from its max |q|);
+    // rows G..7 are zero (the MFMA columns they feed are never read)
+    for (int r = w; r < kMaxGroup; r += 4) {
+        if (r < G) {
+            const uint16_t* qr = a.q + (row0 + r) * kD;
+            float v[4];
+            float mx = 0.0f;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                v[k] = bf16_to_f32(qr[l + 64 * k]);
+                mx = fmaxf(mx, fabsf(v[k]));
+            }
+            for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+            int e;
+            (void)frexpf(mx, &e);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) sm.q[r][l + 64 * k] = ldexpf(v[k], -e);
+            if (l == 0) sm.qe[r] = (float)e;
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) sm.q[r][l + 64 * k] = 0.0f;
+            if (l == 0) sm.qe[r] = 0.0f;
+        }
+    }
+    __syncthreads();
+
+    float M = -INFINITY, lsum = 0.0f;
+    f32x4 O[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) O[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    if (pa < pb) {
+        u32x4 kb[16], vb[16];
+        auto page_base = [&](int p) -> size_t {
+            return (size_t)__builtin_amdgcn_readfirstlane(sm.slot[w][p - pa]) * Hkv + kvh;
+        };
+        {
+            const size_t base = page_base(pa) * (kP * kD);
+            const int8_t* kp = a.kc + base;
+            const int8_t* vp = a.vc + base;
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) kb[4 * s2 + t] = ld16(kp + koff + (4 * t * kD + 64 * s2));
+#pragma unroll
+            for (int j = 0; j < 16; ++j) vb[j] = ld16(vp + voff + 16 * j * kP);
+            const size_t sb = page_base(pa);
+            const u32x4 sk = ld16(a.kchan + sb * kD + 4 * l);
+            const u32x4 sv = ld16(a.vchan + sb * kD + 4 * l);
+            const float st = a.ktok[sb * kP + l];
+            *reinterpret_cast<u32x4*>(&sm.sc[w][0][4 * l]) = sk;
+            *reinterpret_cast<u32x4*>(&sm.sc[w][0][kD + 4 * l]) = sv;
+            sm.sc[w][0][2 * kD + l] = st * a.scale_log2;
+        }
+
+        auto page = [&](auto prefetch, int p) {
+            constexpr bool PF = decltype(prefetch)::value;
+            const int slot = (p - pa) & 1;
+            const float* scl = sm.sc[w][slot];
+            size_t nb = 0, ns = 0;
+            u32x4 skn, svn;
+            float stn = 0.0f;
+            const int8_t* knp = a.kc;
+            const int8_t* vnp = a.vc;
+            if (PF) {
+                ns = page_base(p + 1);
+                nb = ns * (kP * kD);
+                knp = a.kc + nb;
+                vnp = a.vc + nb;
+                skn = ld16(a.kchan + ns * kD + 4 * l);
+                svn = ld16(a.vchan + ns * kD + 4 * l);
+                stn = a.ktok[ns * kP + l];
+            }
+            // S^T over all 256 channels: q' = q (.) c, hi + lo
+            f32x4 S[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) S[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2) {
+                const f32x4* qr = reinterpret_cast<const f32x4*>(&sm.q[hh][64 * s2 + 16 * g]);
+                const f32x4* cr = reinterpret_cast<const f32x4*>(&scl[64 * s2 + 16 * g]);
+                half8 qh[2], ql[2];
+#pragma unroll
+                for (int i4 = 0; i4 < 4; ++i4) {
+                    const f32x4 qq = qr[i4], cc = cr[i4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        _Float16 hi, lo;
+                        split_prod_f16(qq[e], cc[e], hi, lo);
+                        const int i = 4 * i4 + e;
+                        qh[i >> 3][i & 7] = hi;
+                        ql[i >> 3][i & 7] = lo;
+                    }
+                }
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const u32x4 kk = kb[4 * s2 + t];
+                    const half8 a0 = i8x8_to_f16(kk.x, kk.y);
+                    const half8 a1 = i8x8_to_f16(kk.z, kk.w);
+                    S[t] = mfma_f16(a0, qh[0], S[t]);
+                    S[t] = mfma_f16(a0, ql[0], S[t]);
+                    S[t] = mfma_f16(a1, qh[1], S[t]);
+                    S[t] = mfma_f16(a1, ql[1], S[t]);
+                    if (PF) kb[4 * s2 + t] = ld16(knp + koff + (4 * t * kD + 64 * s2));
+                    __builtin_amdgcn_sched_barrier(0);  // keep conversions next to their MFMAs
+                }
+            }
+            // logits (base 2): the token factor multiplies the finished dot product
+            const float qsc = exp2f(sm.qe[hh]);
+            const f32x4* tk = reinterpret_cast<const f32x4*>(&scl[2 * kD + 16 * g]);
+            float z[16], pr[16];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const f32x4 tt = tk[t];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) z[4 * t + r] = S[t][r] * (tt[r] * qsc);
+            }
+            const float alpha = softmax_step_int(z, M, lsum, pr);
+            // every column's rescale factor is exactly 1 on most pages: skip it
+            const bool rescale = __builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0;
+            half8 pbo[2];
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    _Float16 hi, lo;
+                    split_f16(p_elem(pr, s, e), hi, lo);
+                    pbo[s][e] = lo_lane ? lo : hi;
+                }
+            if (rescale) {
+#pragma unroll
+                for (int j = 0; j < 16; ++j) O[j] = O[j] * alpha;
+            }
+            // PV on raw value codes; per-channel value scale at the page boundary
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const u32x4 vv = vb[j];
+                const half8 a0 = i8x8_to_f16(vv.x, vv.y);
+                const half8 a1 = i8x8_to_f16(vv.z, vv.w);
+                f32x4 c = {0.0f, 0.0f, 0.0f, 0.0f};
+                c = mfma_f16(a0, pbo[0], c);
+                c = mfma_f16(a1, pbo[1], c);
+                const f32x4 vs = *reinterpret_cast<const f32x4*>(&scl[kD + 16 * j + 4 * g]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) O[j][r] = O[j][r] + vs[r] * c[r];
+                if (PF) vb[j] = ld16(vnp + voff + 16 * j * kP);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (PF) {
+                float* nsc = sm.sc[w][slot ^ 1];
+                *reinterpret_cast<u32x4*>(&nsc[4 * l]) = skn;
+                *reinterpret_cast<u32x4*>(&nsc[kD + 4 * l]) = svn;
+                nsc[2 * kD + l] = stn * a.scale_log2;
+            }
+        };
+
+        for (int p = pa; p < pb - 1; ++p) page(std::integral_constant<bool, true>(), p);
+        page(std::integral_constant<bool, false>(), pb - 1);
+    }
+
+    // merge the four waves: each publishes its unnormalised O, max and weight sum
+    const float L = group_sum(lsum);
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) O[j][r] += __shfl_xor(O[j][r], 8, 64);
+    if (!lo_lane) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+            *reinterpret_cast<f32x4*>(&sm.mo[w][hh][16 * j + 4 * g]) = O[j];
+        if (g == 0) {
+            sm.mm[w][hh] = M;
+            sm.ml[w][hh] = L;
+        }
+    }
+    __syncthreads();
+    const int d = tid;  // one thread per channel
+    for (int h = 0; h < G; ++h) {
+        float Ms = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) Ms = fmaxf(Ms, sm.mm[k][h]);
+        float lt = 0.0f, ot = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float mk = sm.mm[k][h];
+            if (mk == -INFINITY) continue;
+            const float f = exp2f(mk - Ms);
+            lt += f * sm.ml[k][h];
+            ot += f * sm.mo[k][h][d];
+        }
+        const size_t row = row0 + h;
+        a.part_o[(row * a.n_cols + a.col0 + split) * kD + d] = ot / lt;
+        if (d == 0) a.part_lse[row * a.n_cols + a.col0 + split] = (Ms + log2f(lt)) * kLn2;
+    }
+}
+
+// zero the BF16 elements of an 8-token operand whose token index >= limit
+__device__ __forceinline__ u32x4 mask_tokens(u32x4 v, int first, int limit) {
+    uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t lo_keep = (first + 2 * i < limit) ? 0x0000FFFFu : 0u;
+        const uint32_t hi_keep = (first + 2 * i + 1 < limit) ? 0xFFFF0000u : 0u;
+        wd[i] &= (lo_keep | hi_keep);
+    }
+    return u32x4{wd[0], wd[1], wd[2], wd[3]};
+}
+
+__device__ __forceinline__ void exact_split(const ExactArgs& a, ExactSmem& sm, int split, int kvh, int b) {
+    const int len = a.seq_len[b];
+    const int np = min((len + kP - 1) / kP, a.max_pages);
+    const int p0 = split * a.pps;
+    if (p0 >= np) {
+        write_empty(a.G, a.Hkv, kvh, b, a.n_cols, a.col0 + split, a.part_lse);
+        return;
+    }
+    const int p1 = min(np, p0 + a.pps);
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, n = l & 15, g = l >> 4;
+    const int hh = n & 7;
+    const bool hi_lane = n < 8;
+    const bool valid = hh < a.G;
+    const int Hkv = a.Hkv, Hq = Hkv * a.G;
+    const int32_t* pt = a.page_table + (size_t)b * a.max_pages;
+    const size_t row = (size_t)b * Hq + (size_t)kvh * a.G + hh;
+
+    float (*s_part)[4][16][64] = sm.part;
+
+    // the query is exact in BF16 and needs no per-page work: keep it as the B operand
+    bf16x8 qb[2];
+    {
+        u32x4 q0 = {0, 0, 0, 0}, q1 = {0, 0, 0, 0};
+        if (valid) {
+            const uint16_t* qp = a.q + row * kD + 64 * w + 16 * g;
+            q0 = ld16(qp);
+            q1 = ld16(qp + 8);
+        }
+        qb[0] = as_bf16x8(q0);
+        qb[1] = as_bf16x8(q1);
+    }
+
+    u32x4 kr[8], vr[8];
+    auto load_codes = [&](int p, u32x4 (&K)[8], u32x4 (&V)[8]) {
+        const size_t base = ((size_t)pt[p] * Hkv + kvh) * (kP * kD);
+        const uint16_t* kb = a.kb + base;
+        const uint16_t* vb = a.vb + base;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int s = 0; s < 2; ++s) K[2 * t + s] = ld16(kb + qk_row_token(t, n) * kD + 64 * w + 16 * g + 8 * s);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int s = 0; s < 2; ++s) V[2 * j + s] = ld16(vb + (64 * w + 16 * j + n) * kP + 16 * g + 8 * s);
+    };
+
+    load_codes(p0, kr, vr);
+
+    float M = -INFINITY, lsum = 0.0f;
+    f32x4 O[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) O[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    int it = 0;
+    for (int p = p0; p < p1; ++p, ++it) {
+        const bool has_next = p + 1 < p1;
+        u32x4 kn[8], vn[8];
+        if (has_next) load_codes(p + 1, kn, vn);
+
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+            acc = mfma_bf16(as_bf16x8(kr[2 * t]), qb[0], acc);
+            acc = mfma_bf16(as_bf16x8(kr[2 * t + 1]), qb[1], acc);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s_part[it & 1][w][4 * t + r][l] = acc[r];
+        }
+        __syncthreads();
+
+        const int in_page = len - p * kP;  // valid tokens in this page (>= 1)
+        float S[16], z[16], pr[16];
+        gather_logits(s_part[it & 1], l, S);
+#pragma unroll
+        for (int k = 0; k < 16; ++k) z[k] = (16 * g + k < in_page) ? S[k] * a.scale_log2 : -INFINITY;
+        const float alpha = softmax_step(z, M, lsum, pr);
+
+        bf16x8 pb[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int e2 = 0; e2 < 8; ++e2) {
+                __bf16 hi, lo;
+                split_bf16(p_elem(pr, s, e2), hi, lo);
+                pb[s][e2] = valid ? (hi_lane ? hi : lo) : (__bf16)0.0f;
+            }
+
+        if (in_page < kP) {  // last, partial page: masked values must not reach the MFMA
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int s = 0; s < 2; ++s) vr[2 * j + s] = mask_tokens(vr[2 * j + s], 16 * g + 8 * s, in_page);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            O[j] = O[j] * alpha;
+            O[j] = mfma_bf16(as_bf16x8(vr[2 * j]), pb[0], O[j]);
+            O[j] = mfma_bf16(as_bf16x8(vr[2 * j + 1]), pb[1], O[j]);
+        }
+
+        if (has_next) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                kr[k] = kn[k];
+                vr[k] = vn[k];
+            }
+        }
+    }
+
+    write_partial(O, M, lsum, valid, hi_lane, w, g, row, a.n_cols, a.col0 + split, a.part_o, a.part_lse);
+}
+
+union SplitSmem {
+    Int8Smem i8;
+    ExactSmem ex;
+};
+
+__global__ __launch_bounds__(kThreads, 1) void decode_int8_kernel(Int8Args a) {
+    __shared__ Int8Smem sm;
+    int8_split(a, sm, blockIdx.x, blockIdx.y, blockIdx.z);
+}
+
+__global__ __launch_bounds__(kThreads, 2) void decode_exact_kernel(ExactArgs a) {
+    __shared__ ExactSmem sm;
+    exact_split(a, sm, blockIdx.x, blockIdx.y, blockIdx.z);
+}
+
+// Both tiers of a layer in one launch: splits [0, n8) read int8 pages, the
+// rest read the BF16 window; all write partial columns of the same rows.
+__global__ __launch_bounds__(kThreads, 1) void decode_hybrid_kernel(Int8Args a8, ExactArgs ax, int n8) {
+    __shared__ SplitSmem sm;
+    if ((int)blockIdx.x < n8)
+        int8_split(a8, sm.i8, blockIdx.x, blockIdx.y, blockIdx.z);
+    else
+        exact_split(ax, sm.ex, blockIdx.x - n8, blockIdx.y, blockIdx.z);
+}
+
+static akv_status check_ptrs(const void* const* ptrs, int nptrs) {
+    for (int i = 0; i < nptrs; ++i) {
+        if (!ptrs[i]) return fail(AKV_ERR_ARG, "NULL pointer (argument %d)", i);
+        if (!aligned16(ptrs[i])) return fail(AKV_ERR_ALIGN, "pointer argument %d not 16-byte aligned", i);
+    }
+    return AKV_OK;
+}
+
+static akv_status check_shape(const akv_dims* dims, int32_t batch, int32_t max_pages) {
+    akv_status st = check_dims(dims);
+    if (st != AKV_OK) return st;
+    if (batch < 0 || max_pages < 0) return fail(AKV_ERR_ARG, "negative batch or max_pages");
+    if (batch > 65535) return fail(AKV_ERR_UNSUPPORTED, "batch %d > 65535", batch);
+    return AKV_OK;
+}
+
+static akv_status check_workspace(void* ws, size_t have, size_t need) {
+    if (need == 0) return AKV_OK;
+    if (!ws || have < need) return fail(AKV_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", have, need);
+    if (!aligned16(ws)) return fail(AKV_ERR_ALIGN, "workspace not 16-byte aligned");
+    return AKV_OK;
+}
+
+static void split_workspace(const akv_dims* d, int batch, int n_cols, void* ws, float** po, float** pl) {
+    const size_t rows = (size_t)batch * d->num_kv_heads * d->group;
+    const size_t o = ((rows * n_cols * d->head_dim * sizeof(float) + 255) / 256) * 256;
+    *po = reinterpret_cast<float*>(ws);
+    *pl = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + o);
+}
+
+static Int8Args int8_args(const akv_dims* dims, const uint16_t* q, const int8_t* k_codes, const int8_t* v_codes,
+                          const float* k_chan, const float* k_tok, const float* v_chan, const int32_t* page_table,
+                          const int32_t* n_pages, int max_pages, float scale, const SplitPlan& plan) {
+    Int8Args a;
+    a.q = q;
+    a.kc = k_codes;
+    a.vc = v_codes;
+    a.kchan = k_chan;
+    a.ktok = k_tok;
+    a.vchan = v_chan;
+    a.page_table = page_table;
+    a.n_pages = n_pages;
+    a.max_pages = max_pages;
+    a.Hkv = dims->num_kv_heads;
+    a.G = dims->group;
+    a.pps = plan.pages_per_split;
+    a.col0 = 0;
+    a.n_cols = plan.n_splits;
+    a.scale_log2 = scale * kLog2e;
+    a.part_o = a.part_lse = nullptr;
+    return a;
+}
+
+static ExactArgs exact_args(const akv_dims* dims, const uint16_t* q, const uint16_t* k_bf16, const uint16_t* v_bf16,
+                            const int32_t* page_table, const int32_t* seq_len, int max_pages, float scale,
+                            const SplitPlan& plan) {
+    ExactArgs a;
+    a.q = q;
+    a.kb = k_bf16;
+    a.vb = v_bf16;
+    a.page_table = page_table;
+    a.seq_len = seq_len;
+    a.max_pages = max_pages;
+    a.Hkv = dims->num_kv_heads;
+    a.G = dims->group;
+    a.pps = plan.pages_per_split;
+    a.col0 = 0;
+    a.n_cols = plan.n_splits;
+    a.scale_log2 = scale * kLog2e;
+    a.part_o = a.part_lse = nullptr;
+    return a;
+}
+
+}  // namespace akv
+
+using namespace akv;
+
+extern "C" akv_status akv_decode_attn_int8(const akv_dims* dims, int32_t batch, const uint16_t* q,
+                                           const int8_t* k_codes, const int8_t* v_codes, const float* k_chan,
+                                           const float* k_tok, const float* v_chan, const int32_t* page_table,
+                                           const int32_t* n_pages, int32_t max_pages, float softmax_scale,
+                                           float* out_o, float* out_lse, void* workspace,
+                                           size_t workspace_bytes, void* stream) {
+    clear_error();
+    akv_status st = check_shape(dims, batch, max_pages);
+    if (st != AKV_OK || batch == 0) return st;
+    const void* ptrs[] = {q, k_codes, v_codes, k_chan, k_tok, v_chan, page_table, n_pages, out_o, out_lse};
+    if ((st = check_ptrs(ptrs, 10)) != AKV_OK) return st;
+    const int rows = batch * dims->num_kv_heads * dims->group;
+    if (max_pages == 0) return akv_fill_empty(rows, dims->head_dim, out_o, out_lse, stream);
+    const SplitPlan plan = plan_int8_splits(dims, batch, max_pages);
+    if ((st = check_workspace(workspace, workspace_bytes, partial_bytes(dims, batch, plan.n_splits))) != AKV_OK)
+        return st;
+    hipStream_t s = (hipStream_t)stream;
+    Int8Args a = int8_args(dims, q, k_codes, v_codes, k_chan, k_tok, v_chan, page_table, n_pages, max_pages,
+                           softmax_scale, plan);
+    split_workspace(dims, batch, plan.n_splits, workspace, &a.part_o, &a.part_lse);
+    dim3 grid((unsigned)plan.n_splits, (unsigned)dims->num_kv_heads, (unsigned)batch);
+    prof_begin(s);
+    decode_int8_kernel<<<grid, kThreads, 0, s>>>(a);
+    prof_end(s);
+    if ((st = launch_status("decode_int8_kernel")) != AKV_OK) return st;
+    return launch_combine(rows, dims->head_dim, a.part_o, a.part_lse, plan.n_splits, out_o, out_lse, s);
+}
+
+extern "C" akv_status akv_decode_attn_exact(const akv_dims* dims, int32_t batch, const uint16_t* q,
+                                            const uint16_t* k_bf16, const uint16_t* v_bf16,
+                                            const int32_t* page_table, const int32_t* seq_len, int32_t max_pages,
+                                            float softmax_scale, float* out_o, float* out_lse, void* workspace,
+                                            size_t workspace_bytes, void* stream) {
+    clear_error();
+    akv_status st = check_shape(dims, batch, max_pages);
+    if (st != AKV_OK || batch == 0) return st;
+    const void* ptrs[] = {q, k_bf16, v_bf16, page_table, seq_len, out_o, out_lse};
+    if ((st = check_ptrs(ptrs, 7)) != AKV_OK) return st;
+    const int rows = batch * dims->num_kv_heads * dims->group;
+    if (max_pages == 0) return akv_fill_empty(rows, dims->head_dim, out_o, out_lse, stream);
+    const SplitPlan plan = plan_splits(dims, batch, max_pages);
+    if ((st = check_workspace(workspace, workspace_bytes, partial_bytes(dims, batch, plan.n_splits))) != AKV_OK)
+        return st;
+    hipStream_t s = (hipStream_t)stream;
+    ExactArgs a = exact_args(dims, q, k_bf16, v_bf16, page_table, seq_len, max_pages, softmax_scale, plan);
+    split_workspace(dims, batch, plan.n_splits, workspace, &a.part_o, &a.part_lse);
+    dim3 grid((unsigned)plan.n_splits, (unsigned)dims->num_kv_heads, (unsigned)batch);
+    prof_begin(s);
+    decode_exact_kernel<<<grid, kThreads, 0, s>>>(a);
+    prof_end(s);
+    if ((st = launch_status("decode_exact_kernel")) != AKV_OK) return st;
+    return launch_combine(rows, dims->head_dim, a.part_o, a.part_lse, plan.n_splits, out_o, out_lse, s);
+}
+
+extern "C" akv_status akv_decode_hybrid(const akv_dims* dims, int32_t batch, const uint16_t* q,
+                                        const int8_t* k_codes, const int8_t* v_codes, const float* k_chan,
+                                        const float* k_tok, const float* v_chan, const int32_t* page_table_int8,
+                                        const int32_t* n_pages_int8, int32_t max_pages_int8, const uint16_t* k_bf16,
+                                        const uint16_t* v_bf16, const int32_t* page_table_window,
+                                        const int32_t* window_len, int32_t max_pages_window, float softmax_scale,
+                                        float* out_o, float* out_lse, void* workspace, size_t workspace_bytes,
+                                        void* stream) {
+    clear_error();
+    akv_status st = check_shape(dims, batch, max_pages_int8);
+    if (st != AKV_OK) return st;
+    if (max_pages_window < 0) return fail(AKV_ERR_ARG, "negative max_pages_window");
+    if (batch == 0) return AKV_OK;
+    const void* ptrs[] = {q, k_codes, v_codes, k_chan, k_tok, v_chan, page_table_int8, n_pages_int8,
+                          k_bf16, v_bf16, page_table_window, window_len, out_o, out_lse};
+    if ((st = check_ptrs(ptrs, 14)) != AKV_OK) return st;
+    const int rows = batch * dims->num_kv_heads * dims->group;
+    if (max_pages_int8 + max_pages_window == 0) return akv_fill_empty(rows, dims->head_dim, out_o, out_lse, stream);
+    const SplitPlan p8 = plan_int8_splits(dims, batch, max_pages_int8);
+    const SplitPlan pw = plan_window_splits(dims, batch, max_pages_window);
+    const int n_cols = p8.n_splits + pw.n_splits;
+    if ((st = check_workspace(workspace, workspace_bytes, partial_bytes(dims, batch, n_cols))) != AKV_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    Int8Args a8 = int8_args(dims, q, k_codes, v_codes, k_chan, k_tok, v_chan, page_table_int8, n_pages_int8,
+                            max_pages_int8, softmax_scale, p8);
+    ExactArgs ax = exact_args(dims, q, k_bf16, v_bf16, page_table_window, window_len, max_pages_window,
+                              softmax_scale, pw);
+    a8.n_cols = ax.n_cols = n_cols;
+    ax.col0 = p8.n_splits;
+    split_workspace(dims, batch, n_cols, workspace, &a8.part_o, &a8.part_lse);
+    ax.part_o = a8.part_o;
+    ax.part_lse = a8.part_lse;
+    dim3 grid((unsigned)n_cols, (unsigned)dims->num_kv_heads, (unsigned)batch);
+    prof_begin(s);
+    decode_hybrid_kernel<<<grid, kThreads, 0, s>>>(a8, ax, p8.n_splits);
+    prof_end(s);
+    if ((st = launch_status("decode_hybrid_kernel")) != AKV_OK) return st;
+    return launch_combine(rows, dims->head_dim, a8.part_o, a8.part_lse, n_cols, out_o, out_lse, s);
+}

@@ -1,0 +1,169 @@
+// merge.hip -- exact log-sum-exp merges ("SYCL" page, "A merge that joins
+// the tiers": partials fold into one FP32 accumulator, an LSE of -inf is a
+// valid empty partial).
+//
+// akv_merge_lse: one work-group per row (a request's query head), one thread
+// per channel.  The split-K second pass (combine_kernel) uses the same rule
+// over all of a row's split partials.
+#include <math.h>
+
+#include "akv_device.h"
+#include "akv_host.h"
+
+namespace akv {
+
+__global__ void fill_empty_kernel(int rows, int D, float* __restrict__ o, float* __restrict__ lse) {
+    const size_t total = (size_t)rows * D;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (size_t)gridDim.x * blockDim.x)
+        o[i] = 0.0f;
+    for (size_t r = (size_t)blockIdx.x * blockDim.x + threadIdx.x; r < (size_t)rows;
+         r += (size_t)gridDim.x * blockDim.x)
+        lse[r] = -INFINITY;
+}
+
+// acc <- acc (+) part, exactly, per row.
+__global__ void merge_lse_kernel(int D, float* __restrict__ acc_o, float* __restrict__ acc_lse,
+                                 const float* __restrict__ part_o, const float* __restrict__ part_lse) {
+    const int r = blockIdx.x;
+    const float a = acc_lse[r], p = part_lse[r];
+    const float m = fmaxf(a, p);
+    float wa = 0.0f, wp = 0.0f, L = -INFINITY;
+    if (m != -INFINITY) {
+        const float ea = (a == -INFINITY) ? 0.0f : expf(a - m);
+        const float ep = (p == -INFINITY) ? 0.0f : expf(p - m);
+        const float s = ea + ep;
+        L = m + logf(s);
+        wa = ea / s;
+        wp = ep / s;
+    }
+    __syncthreads();  // every thread has read acc_lse[r] before it is rewritten
+    for (int d = threadIdx.x; d < D; d += blockDim.x) {
+        const size_t i = (size_t)r * D + d;
+        // an empty side contributes nothing, whatever its O holds
+        float v = 0.0f;
+        if (wa != 0.0f) v += wa * acc_o[i];
+        if (wp != 0.0f) v += wp * part_o[i];
+        acc_o[i] = v;
+    }
+    if (threadIdx.x == 0) acc_lse[r] = L;
+}
+
+// Split-K second pass.  Row r = b*Hq + j holds n_splits partials
+// part_o[r][s][D], part_lse[r][s]; every split slot is written by the split
+// pass on every call (an empty split writes LSE = -inf), so no counts are
+// needed here.  Block (r, c) owns channels [32c, 32c + 32): 8 split lanes x
+// 32 channels, the LSE statistics are block-reduced once.
+__device__ __forceinline__ float block_reduce_max(float v, float* red) {
+    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    v = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    __syncthreads();
+    return v;
+}
+__device__ __forceinline__ float block_reduce_sum(float v, float* red) {
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    v = (red[0] + red[1]) + (red[2] + red[3]);
+    __syncthreads();
+    return v;
+}
+
+constexpr int kCombineMaxSplits = 2048;  // weights staged in LDS; larger counts loop in chunks
+
+__global__ __launch_bounds__(256) void combine_kernel(int D, int n_splits, const float* __restrict__ part_o,
+                                                      const float* __restrict__ part_lse, float* __restrict__ out_o,
+                                                      float* __restrict__ out_lse) {
+    const int r = blockIdx.x, chunk = blockIdx.y;
+    const int tid = threadIdx.x, sl = tid >> 5, c = tid & 31;
+    __shared__ float red[4];
+    __shared__ float wgt[kCombineMaxSplits];
+    __shared__ float acc_s[8][32];
+    const float* lse = part_lse + (size_t)r * n_splits;
+    float m = -INFINITY;
+    for (int s = tid; s < n_splits; s += 256) m = fmaxf(m, lse[s]);
+    m = block_reduce_max(m, red);
+    const int d = chunk * 32 + c;
+    if (m == -INFINITY) {
+        if (sl == 0) out_o[(size_t)r * D + d] = 0.0f;
+        if (chunk == 0 && tid == 0) out_lse[r] = -INFINITY;
+        return;
+    }
+    float sum = 0.0f;
+    float acc = 0.0f;
+    const float* po = part_o + (size_t)r * n_splits * D + d;
+    for (int base = 0; base < n_splits; base += kCombineMaxSplits) {
+        const int cnt = min(kCombineMaxSplits, n_splits - base);
+        for (int s = tid; s < cnt; s += 256) {
+            const float l = lse[base + s];
+            const float e = (l == -INFINITY) ? 0.0f : expf(l - m);
+            wgt[s] = e;
+            sum += e;
+        }
+        __syncthreads();
+        // 8 split lanes x 32 channels; independent loads, a zero weight skips nothing
+        // (an empty split's O slot may hold anything, so it is masked, not multiplied)
+        int s = sl;
+        for (; s + 24 < cnt; s += 32) {
+            const float w0 = wgt[s], w1 = wgt[s + 8], w2 = wgt[s + 16], w3 = wgt[s + 24];
+            const float o0 = po[(size_t)(base + s) * D], o1 = po[(size_t)(base + s + 8) * D];
+            const float o2 = po[(size_t)(base + s + 16) * D], o3 = po[(size_t)(base + s + 24) * D];
+            acc += (w0 != 0.0f ? w0 * o0 : 0.0f) + (w1 != 0.0f ? w1 * o1 : 0.0f) +
+                   (w2 != 0.0f ? w2 * o2 : 0.0f) + (w3 != 0.0f ? w3 * o3 : 0.0f);
+        }
+        for (; s < cnt; s += 8) {
+            const float w0 = wgt[s];
+            if (w0 != 0.0f) acc += w0 * po[(size_t)(base + s) * D];
+        }
+        __syncthreads();
+    }
+    sum = block_reduce_sum(sum, red);
+    acc_s[sl][c] = acc;
+    __syncthreads();
+    if (sl == 0) {
+        float t = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) t += acc_s[k][c];
+        out_o[(size_t)r * D + d] = t / sum;
+    }
+    if (chunk == 0 && tid == 0) out_lse[r] = m + logf(sum);
+}
+
+akv_status launch_combine(int rows, int D, const float* part_o, const float* part_lse, int n_splits, float* out_o,
+                          float* out_lse, hipStream_t stream) {
+    if (rows == 0) return AKV_OK;
+    dim3 grid((unsigned)rows, (unsigned)(D / 32));
+    combine_kernel<<<grid, 256, 0, stream>>>(D, n_splits, part_o, part_lse, out_o, out_lse);
+    return launch_status("combine_kernel");
+}
+
+}  // namespace akv
+
+using namespace akv;
+
+extern "C" akv_status akv_fill_empty(int32_t rows, int32_t head_dim, float* o, float* lse, void* stream) {
+    clear_error();
+    if (rows < 0 || head_dim < 0) return fail(AKV_ERR_ARG, "negative size");
+    if (rows == 0) return AKV_OK;
+    if (!o || !lse) return fail(AKV_ERR_ARG, "NULL pointer");
+    if (!aligned16(o) || !aligned16(lse)) return fail(AKV_ERR_ALIGN, "o/lse not 16-byte aligned");
+    const size_t total = (size_t)rows * head_dim;
+    int blocks = (int)std::min<size_t>((total + 255) / 256, 4096);
+    if (blocks < 1) blocks = 1;
+    fill_empty_kernel<<<blocks, 256, 0, (hipStream_t)stream>>>(rows, head_dim, o, lse);
+    return launch_status("fill_empty_kernel");
+}
+
+extern "C" akv_status akv_merge_lse(int32_t rows, int32_t head_dim, float* acc_o, float* acc_lse,
+                                    const float* part_o, const float* part_lse, void* stream) {
+    clear_error();
+    if (rows < 0 || head_dim < 0) return fail(AKV_ERR_ARG, "negative size");
+    if (rows == 0) return AKV_OK;
+    if (!acc_o || !acc_lse || !part_o || !part_lse) return fail(AKV_ERR_ARG, "NULL pointer");
+    if (!aligned16(acc_o) || !aligned16(acc_lse) || !aligned16(part_o) || !aligned16(part_lse))
+        return fail(AKV_ERR_ALIGN, "tensor not 16-byte aligned");
+    merge_lse_kernel<<<rows, 256, 0, (hipStream_t)stream>>>(head_dim, acc_o, acc_lse, part_o, part_lse);
+    return launch_status("merge_lse_kernel");
+}

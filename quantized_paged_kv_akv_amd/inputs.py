@@ -256,3 +256,28 @@ def make_layer_torch(w: Workload, layer: int, device, plan: Optional[PoolPlan] =
         del K, V
     q = torch.randn((w.batch, w.num_q_heads, D), device=device, generator=gen(0, layer, T_Q)).to(torch.bfloat16)
     return dict(q=q, k_pool=kpool, v_pool=vpool, plan=plan)
+
+
+# --------------------------------------------------------------------------- free-form pools
+def random_pools(seed: int, n_slots: int, Hkv: int, outlier_frac: float = 0.02,
+                 k_std=(0.1, 10.0), v_std=(0.5, 2.0)):
+    """BF16 K [S][Hkv][P][D] and V [S][Hkv][D][P] pools of whole random pages
+    with the workload's distributions (per-channel log-uniform std, a fraction
+    of token rows x8).  For tests that need arbitrary page counts."""
+    import math
+    r = np.random.default_rng(seed)
+    P, D = 64, 256
+    sk = np.exp(r.uniform(math.log(k_std[0]), math.log(k_std[1]), (1, Hkv, 1, D))).astype(np.float32)
+    sv = np.exp(r.uniform(math.log(v_std[0]), math.log(v_std[1]), (1, Hkv, D, 1))).astype(np.float32)
+    K = r.standard_normal((n_slots, Hkv, P, D), dtype=np.float32) * sk
+    V = r.standard_normal((n_slots, Hkv, D, P), dtype=np.float32) * sv
+    if outlier_frac > 0:
+        s_idx, t_idx = np.nonzero(r.random((n_slots, P)) < outlier_frac)
+        K[s_idx, :, t_idx, :] *= np.float32(8.0)
+        V[s_idx, :, :, t_idx] *= np.float32(8.0)
+    return f32_to_bf16_bits(K), f32_to_bf16_bits(V)
+
+
+def random_queries(seed: int, batch: int, Hq: int, D: int = 256, scale: float = 1.0) -> np.ndarray:
+    r = np.random.default_rng(seed)
+    return f32_to_bf16_bits(r.standard_normal((batch, Hq, D), dtype=np.float32) * np.float32(scale))

@@ -1,0 +1,79 @@
+"""The C-ABI library loads and exports every function include/akv.h declares;
+host-side argument checks answer without touching a GPU."""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "quantized_paged_kv_akv_amd", "libakv.so")
+
+
+@pytest.fixture(scope="module")
+def B():
+    if not os.path.exists(LIB):
+        from quantized_paged_kv_akv_amd import build
+        build.build()
+    from quantized_paged_kv_akv_amd import binding
+    return binding
+
+
+def test_exports_every_declared_symbol(B):
+    names = B.header_functions()
+    assert len(names) >= 13
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    lib = ctypes.CDLL(LIB)
+    for n in names:
+        getattr(lib, n)
+
+
+def test_status_strings_and_version(B):
+    for code, name in B.STATUS.items():
+        assert B._lib.akv_status_string(code).decode() == name
+    assert B.version().startswith("akv ")
+
+
+def test_host_side_validation(B):
+    lib = B._lib
+    d = B.dims(4, 6)
+    # unsupported shapes and bad arguments are refused before any GPU work
+    assert lib.akv_quantize_pages(None, 1, *([None] * 9), None) == -1
+    bad = B.dims(4, 6, head_dim=128)
+    assert lib.akv_quantize_pages(ctypes.byref(bad), 1, *([None] * 9), None) == -2
+    assert "head_dim" in lib.akv_last_error().decode()
+    g9 = B.dims(1, 9)
+    assert lib.akv_quantize_pages(ctypes.byref(g9), 1, *([None] * 9), None) == -2
+    assert lib.akv_quantize_pages(ctypes.byref(d), -1, *([None] * 9), None) == -1
+    assert lib.akv_quantize_pages(ctypes.byref(d), 0, *([None] * 9), None) == 0
+    assert lib.akv_merge_lse(-1, 256, None, None, None, None, None) == -1
+    assert lib.akv_merge_lse(4, 256, None, None, None, None, None) == -1
+    assert lib.akv_fill_empty(0, 256, None, None, None) == 0
+    # misaligned pointer
+    assert lib.akv_merge_lse(1, 256, 8, 16, 16, 16, None) == -3
+    # workspace too small
+    ws = B.akv_decode_workspace_bytes(d, 1, 2032)
+    assert ws > 0 and B.akv_decode_workspace_bytes(d, 0, 10) == 0
+    p = ctypes.c_void_p(16)
+    st = lib.akv_decode_attn_int8(ctypes.byref(d), 1, p, p, p, p, p, p, p, p, 2032, 0.0625, p, p, p, 16, None)
+    assert st == -4
+    st = lib.akv_decode_attn_exact(ctypes.byref(d), 1, p, p, p, p, p, 2032, 0.0625, p, p, p, 16, None)
+    assert st == -4
+    # ring refuses fewer than 2 slots and NULL slots
+    h = ctypes.c_void_p()
+    arr = (ctypes.c_void_p * 1)(ctypes.c_void_p(16))
+    assert lib.akv_ring_create(arr, 1024, 1, ctypes.byref(h)) == -1
+    arr2 = (ctypes.c_void_p * 2)(ctypes.c_void_p(16), ctypes.c_void_p(0))
+    assert lib.akv_ring_create(arr2, 1024, 2, ctypes.byref(h)) == -1
+
+
+def test_workspace_is_deterministic_and_covers_splits(B):
+    d = B.dims(4, 6)
+    for batch, mp in [(1, 2032), (1, 496), (32, 256), (2, 17), (1, 1)]:
+        a = B.akv_decode_workspace_bytes(d, batch, mp)
+        assert a == B.akv_decode_workspace_bytes(d, batch, mp)
+        # at least one partial row per (request, query head)
+        assert a >= batch * 24 * (256 + 1) * 4
