@@ -254,6 +254,40 @@ def cpu_baseline(w):
                 wall_s=wall)
 
 
+def profile_kernels(args, w):
+    """Kernel sequence for rocprofv3 counter passes: a plain 1 GiB device copy
+    (known bytes, to calibrate FETCH_SIZE / WRITE_SIZE), then `steps` hybrid
+    decode steps of the workload."""
+    import torch
+
+    from quantized_paged_kv_akv_amd import binding as B
+    from quantized_paged_kv_akv_amd import configs
+
+    device = torch.device("cuda", 0)
+    plan, layers, T, _, _ = build_layers(w, device)
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=device)
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log("[profile] 3 x 1 GiB device copy done")
+    dims = B.dims(w.num_kv_heads, w.group)
+    m8, mw = T["t8"].shape[1], T["tw"].shape[1]
+    ws = torch.empty(max(16, B.akv_decode_hybrid_workspace_bytes(dims, w.batch, m8, mw)), dtype=torch.uint8,
+                     device=device)
+    o = torch.empty((w.batch, w.num_q_heads, w.head_dim), device=device)
+    lse = torch.empty((w.batch, w.num_q_heads), device=device)
+    for _ in range(args.steps):
+        for L in layers:
+            B.akv_decode_hybrid(dims, w.batch, L["q"], L["k_codes"], L["v_codes"], L["k_chan"], L["k_tok"],
+                                L["v_chan"], T["t8"], T["n8"], m8, L["k_pool"], L["v_pool"], T["tw"], T["nw"], mw,
+                                configs.SIGMA, o, lse, ws)
+    torch.cuda.synchronize()
+    log(f"[profile] {args.steps} hybrid steps done")
+
+
 def load_traffic(kernel: str, workload: str):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
     taken on the current kernel source."""
@@ -276,6 +310,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="ctx128k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-kernels", action="store_true",
+                    help="for counter runs: a 1 GiB device copy (calibration), then --steps hybrid steps; no JSON")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only (the path is measured on one GPU's share; "
@@ -284,6 +320,9 @@ def main():
 
     from quantized_paged_kv_akv_amd import configs
     w = configs.ALL[args.workload]()
+    if args.profile_kernels:
+        profile_kernels(args, w)
+        return
     r = run_gpu(args, w)
     ms = r["ms_hybrid"]
     value = r["hybrid_bytes"] / (ms * 1e-3) / 1e9

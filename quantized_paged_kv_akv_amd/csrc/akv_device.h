@@ -20,6 +20,7 @@ constexpr int kMaxGroup = 8;
 constexpr int kThreads = 256;  // 4 waves; wave w owns channels [64w, 64w + 64)
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -81,6 +82,19 @@ __device__ __forceinline__ void split_prod_f16(float a, float b, _Float16& hi, _
     asm volatile("" : "+v"(x));  // x is a rounded FP32 value: no mixed-precision fusion through it
     hi = (_Float16)x;
     lo = (_Float16)(x - (float)hi);
+}
+// Two at a time with the packed conversions (v_cvt_pk_f16_f32).
+__device__ __forceinline__ void split_prod_f16x2(float a0, float b0, float a1, float b1, half2& hi, half2& lo) {
+#pragma clang fp contract(off)
+    float x0 = a0 * b0, x1 = a1 * b1;
+    asm volatile("" : "+v"(x0), "+v"(x1));
+    hi = half2{(_Float16)x0, (_Float16)x1};
+    lo = half2{(_Float16)(x0 - (float)hi[0]), (_Float16)(x1 - (float)hi[1])};
+}
+__device__ __forceinline__ void split_f16x2(float x0, float x1, half2& hi, half2& lo) {
+#pragma clang fp contract(off)
+    hi = half2{(_Float16)x0, (_Float16)x1};
+    lo = half2{(_Float16)(x0 - (float)hi[0]), (_Float16)(x1 - (float)hi[1])};
 }
 __device__ __forceinline__ void split_f16(float x, _Float16& hi, _Float16& lo) {
 #pragma clang fp contract(off)

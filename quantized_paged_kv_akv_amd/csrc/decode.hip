@@ -180,11 +180,11 @@ __device__ __forceinline__ void write_empty(int G, int Hkv, int kvh, int b, int 
 constexpr int kMaxPagesPerWave = 64;
 
 struct Int8Smem {
-    float q[kMaxGroup][kD];        // query rows (scaled by 2^-e per row), FP32
+    float q[kMaxGroup][kD + 4];    // query rows (scaled by 2^-e per row), FP32; +4 spreads rows over banks
     float qe[kMaxGroup];           // the row's power-of-two exponent e
     float sc[4][2][2 * kD + kP];   // per wave, per slot: k_chan | v_chan | k_tok * scale_log2
     int slot[4][kMaxPagesPerWave]; // pool slots of each wave's pages
-    float mo[4][kMaxGroup][kD];    // end merge: each wave's unnormalised O
+    float mo[4][kMaxGroup][kD + 4];  // end merge: each wave's unnormalised O (padded like q)
     float mm[4][kMaxGroup];        // ... its running max (base 2)
     float ml[4][kMaxGroup];        // ... its sum of weights
 };
@@ -298,12 +298,14 @@ __device__ __forceinline__ void int8_split(const Int8Args& a, Int8Smem& sm, int 
                 for (int i4 = 0; i4 < 4; ++i4) {
                     const f32x4 qq = qr[i4], cc = cr[i4];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        _Float16 hi, lo;
-                        split_prod_f16(qq[e], cc[e], hi, lo);
+                    for (int e = 0; e < 4; e += 2) {
+                        half2 hi, lo;
+                        split_prod_f16x2(qq[e], cc[e], qq[e + 1], cc[e + 1], hi, lo);
                         const int i = 4 * i4 + e;
-                        qh[i >> 3][i & 7] = hi;
-                        ql[i >> 3][i & 7] = lo;
+                        qh[i >> 3][i & 7] = hi[0];
+                        qh[i >> 3][(i & 7) + 1] = hi[1];
+                        ql[i >> 3][i & 7] = lo[0];
+                        ql[i >> 3][(i & 7) + 1] = lo[1];
                     }
                 }
 #pragma unroll
@@ -336,10 +338,12 @@ __device__ __forceinline__ void int8_split(const Int8Args& a, Int8Smem& sm, int 
 #pragma unroll
             for (int s = 0; s < 2; ++s)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    _Float16 hi, lo;
-                    split_f16(p_elem(pr, s, e), hi, lo);
-                    pbo[s][e] = lo_lane ? lo : hi;
+                for (int e = 0; e < 8; e += 2) {
+                    half2 hi, lo;
+                    split_f16x2(p_elem(pr, s, e), p_elem(pr, s, e + 1), hi, lo);
+                    const half2 v = lo_lane ? lo : hi;
+                    pbo[s][e] = v[0];
+                    pbo[s][e + 1] = v[1];
                 }
             if (rescale) {
 #pragma unroll
