@@ -62,21 +62,22 @@ SplitPlan plan_splits(const akv_dims* d, int batch, int max_pages) {
     return p;
 }
 
-// One wave per SIMD is resident (1024 on the chip); give each about an equal
+// Two waves per SIMD are resident (2048 on the chip); give each about an equal
 // share of the page-heads, at least 2 pages so the per-wave set-up and the
-// end-of-split merge stay small.  AKV_PAGES_PER_WAVE overrides (sweeps).
+// end-of-split merge stay small.  A work-group is four waves, so it owns four
+// waves' worth of consecutive pages.  AKV_PAGES_PER_WAVE overrides (sweeps).
 SplitPlan plan_int8_splits(const akv_dims* d, int batch, int max_pages) {
     SplitPlan p{1, 0};
     if (batch <= 0 || max_pages <= 0) return p;
     long long units = (long long)batch * d->num_kv_heads * max_pages;
-    int ppw = (int)std::max<long long>(2, (units + 1023) / 1024);
+    int ppw = (int)std::max<long long>(2, (units + 2047) / 2048);
     if (const char* e = getenv("AKV_PAGES_PER_WAVE")) {
         int v = atoi(e);
         if (v > 0) ppw = v;
     }
-    ppw = std::min(std::min(ppw, max_pages), 64);  // a wave stages at most 64 page slots
-    p.pages_per_split = ppw;
-    p.n_splits = (max_pages + 4 * ppw - 1) / (4 * ppw);
+    ppw = std::min(ppw, kMaxPagesPerWave);
+    p.pages_per_split = std::min(4 * ppw, max_pages);
+    p.n_splits = (max_pages + p.pages_per_split - 1) / p.pages_per_split;
     return p;
 }
 
@@ -89,6 +90,56 @@ SplitPlan plan_window_splits(const akv_dims* d, int batch, int max_pages) {
     p.pages_per_split = pps;
     p.n_splits = (max_pages + pps - 1) / pps;
     return p;
+}
+
+int device_cu_count() {
+    static thread_local int cached_dev = -1, cached_cus = 256;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    if (dev != cached_dev) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
+            cached_cus = cus;
+        else
+            (void)hipGetLastError();
+        cached_dev = dev;
+    }
+    return cached_cus;
+}
+
+static int env_int(const char* name) {
+    const char* e = getenv(name);
+    return e ? atoi(e) : 0;
+}
+
+void plan_hybrid(const akv_dims* d, int batch, int max_pages_int8, int max_pages_window, SplitPlan* p8,
+                 SplitPlan* pw) {
+    *p8 = plan_int8_splits(d, batch, max_pages_int8);
+    *pw = plan_window_splits(d, batch, max_pages_window);
+    if (batch <= 0 || max_pages_window <= 0 || max_pages_int8 <= 0) return;
+    const long long units = (long long)batch * d->num_kv_heads;
+    const long long slots = 2LL * device_cu_count();
+    // A BF16 page is twice the bytes of an int8 page: a window work-group of
+    // half as many pages streams as long as an int8 one.
+    int qw = std::max(1, std::min(p8->pages_per_split / 2, max_pages_window));
+    const long long nw = units * ((max_pages_window + qw - 1) / qw);
+    const long long n8 = units * p8->n_splits;
+    // A grid a little over one round would leave a few int8 work-groups to run
+    // after all the others: widen the int8 work-groups until it fits.
+    if (n8 + nw > slots && 4 * (n8 + nw) <= 5 * slots && slots - nw >= units) {
+        const int splits = (int)((slots - nw) / units);
+        const int q8 = (max_pages_int8 + splits - 1) / splits;
+        if ((q8 + 3) / 4 <= kMaxPagesPerWave) *p8 = SplitPlan{q8, (max_pages_int8 + q8 - 1) / q8};
+    }
+    if (int v = env_int("AKV_HYBRID_INT8_PAGES")) *p8 = SplitPlan{std::min(v, 4 * kMaxPagesPerWave), 0};
+    if (int v = env_int("AKV_HYBRID_WINDOW_PAGES")) qw = v;
+    p8->pages_per_split = std::min(p8->pages_per_split, max_pages_int8);
+    p8->n_splits = (max_pages_int8 + p8->pages_per_split - 1) / p8->pages_per_split;
+    qw = std::min(qw, max_pages_window);
+    *pw = SplitPlan{qw, (max_pages_window + qw - 1) / qw};
 }
 
 size_t partial_bytes(const akv_dims* d, int batch, int n_splits) {
@@ -138,7 +189,7 @@ extern "C" size_t akv_decode_hybrid_workspace_bytes(const akv_dims* dims, int32_
                                                     int32_t max_pages_window) {
     if (akv::check_dims(dims) != AKV_OK || batch <= 0 || max_pages_int8 < 0 || max_pages_window < 0) return 0;
     if (max_pages_int8 + max_pages_window == 0) return 0;
-    akv::SplitPlan p8 = akv::plan_int8_splits(dims, batch, max_pages_int8);
-    akv::SplitPlan pw = akv::plan_window_splits(dims, batch, max_pages_window);
+    akv::SplitPlan p8, pw;
+    akv::plan_hybrid(dims, batch, max_pages_int8, max_pages_window, &p8, &pw);
     return akv::partial_bytes(dims, batch, p8.n_splits + pw.n_splits);
 }

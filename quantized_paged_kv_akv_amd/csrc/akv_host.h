@@ -32,8 +32,10 @@ struct SplitPlan {
 };
 SplitPlan plan_splits(const akv_dims* d, int batch, int max_pages);
 
-// Plan of the int8 tier, whose work-groups are four waves that each own
-// pages_per_split consecutive pages: n_splits = ceil(max_pages / (4 * pps)).
+// Plan of the int8 tier: a work-group owns pages_per_split consecutive pages
+// and splits them near-evenly over its four waves, each of which stages at
+// most kMaxPagesPerWave page slots.
+constexpr int kMaxPagesPerWave = 64;
 SplitPlan plan_int8_splits(const akv_dims* d, int batch, int max_pages);
 
 // Workspace bytes for `batch` requests with `n_splits` splits each.
@@ -42,6 +44,17 @@ size_t partial_bytes(const akv_dims* d, int batch, int n_splits);
 // Split plan for the recent window of the hybrid call: few pages per split so
 // the window's work-groups spread across the chip next to the int8 ones.
 SplitPlan plan_window_splits(const akv_dims* d, int batch, int max_pages);
+
+// Both tiers of akv_decode_hybrid: window work-groups stream about as many
+// bytes as int8 ones, and when the grid would spill just past one round of
+// resident work-groups (two per compute unit) the int8 work-groups widen so
+// that it fits.  AKV_HYBRID_INT8_PAGES / AKV_HYBRID_WINDOW_PAGES override the
+// pages per work-group of each tier (launch-shape sweeps).
+void plan_hybrid(const akv_dims* d, int batch, int max_pages_int8, int max_pages_window, SplitPlan* p8,
+                 SplitPlan* pw);
+
+// Compute units of the current device (256 if it cannot be queried).
+int device_cu_count();
 
 inline akv_status launch_status(const char* what) {
     hipError_t e = hipGetLastError();

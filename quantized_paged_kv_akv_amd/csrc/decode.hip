@@ -177,8 +177,6 @@ __device__ __forceinline__ void write_empty(int G, int Hkv, int kvh, int b, int 
 // go to the other half of a per-wave LDS double buffer.  The four waves of a
 // work-group take consecutive page ranges of one (request, KV head) and merge
 // once at the end.
-constexpr int kMaxPagesPerWave = 64;
-
 struct Int8Smem {
     float q[kMaxGroup][kD + 4];    // query rows (scaled by 2^-e per row), FP32; +4 spreads rows over banks
     float qe[kMaxGroup];           // the row's power-of-two exponent e
@@ -191,23 +189,42 @@ struct Int8Smem {
 
 __device__ __forceinline__ void int8_split(const Int8Args& a, Int8Smem& sm, int split, int kvh, int b) {
     const int np = min(a.n_pages[b], a.max_pages);
-    const int ppw = a.pps;  // pages per wave
-    const int wg0 = split * 4 * ppw;
+    const int wg0 = split * a.pps;  // this work-group's pages [wg0, wg1)
     if (wg0 >= np) {
         write_empty(a.G, a.Hkv, kvh, b, a.n_cols, a.col0 + split, a.part_lse);
         return;
     }
+    const int len = min(np, wg0 + a.pps) - wg0;
     const int tid = threadIdx.x, l = tid & 63, n = l & 15, g = l >> 4;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int G = a.G, Hkv = a.Hkv, Hq = Hkv * G;
     const int hh = n & 7;
     const bool lo_lane = n >= 8;
-    const int pa = min(np, wg0 + w * ppw), pb = min(np, wg0 + (w + 1) * ppw);
+    // the four waves take near-equal consecutive shares of the range
+    const int pa = wg0 + (w * len) / 4, pb = wg0 + ((w + 1) * len) / 4;
     // per-lane byte offsets inside a page; tile offsets are immediates
     const uint32_t koff = (uint32_t)(qk_row_token(0, n) * kD + 16 * g);
     const uint32_t voff = (uint32_t)(n * kP + 16 * g);
     const int32_t* pt = a.page_table + (size_t)b * a.max_pages;
     const size_t row0 = (size_t)b * Hq + (size_t)kvh * G;
+
+    // The first page's codes and scales are requested before anything else, so
+    // the memory pipeline starts with the work-group; the query staging and the
+    // barrier below overlap their latency.
+    u32x4 buf[16];
+    u32x4 sk0 = {0, 0, 0, 0}, sv0 = {0, 0, 0, 0};
+    float st0 = 0.0f;
+    if (pa < pb) {
+        const size_t sb = (size_t)__builtin_amdgcn_readfirstlane(pt[pa]) * Hkv + kvh;
+        const int8_t* kp = a.kc + sb * (kP * kD);
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) buf[4 * s2 + t] = ld16(kp + koff + (4 * t * kD + 64 * s2));
+        sk0 = ld16(a.kchan + sb * kD + 4 * l);
+        sv0 = ld16(a.vchan + sb * kD + 4 * l);
+        st0 = a.ktok[sb * kP + l];
+    }
 
     // this wave's page slots, read once (the loop reads them from LDS)
     for (int i = l; i < pb - pa; i += 64) sm.slot[w][i] = pt[pa + i];
@@ -215,26 +232,19 @@ __device__ __forceinline__ void int8_split(const Int8Args& a, Int8Smem& sm, int 
     // query rows of this KV head, FP32, each scaled by 2^-e (e from its max |q|);
     // rows G..7 are zero (the MFMA columns they feed are never read)
     for (int r = w; r < kMaxGroup; r += 4) {
+        f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+        int e = 0;
         if (r < G) {
-            const uint16_t* qr = a.q + (row0 + r) * kD;
-            float v[4];
-            float mx = 0.0f;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                v[k] = bf16_to_f32(qr[l + 64 * k]);
-                mx = fmaxf(mx, fabsf(v[k]));
-            }
+            const u32x2 raw = *reinterpret_cast<const u32x2*>(a.q + (row0 + r) * kD + 4 * l);
+            v = f32x4{bf16_to_f32((uint16_t)(raw.x & 0xFFFFu)), bf16_to_f32((uint16_t)(raw.x >> 16)),
+                      bf16_to_f32((uint16_t)(raw.y & 0xFFFFu)), bf16_to_f32((uint16_t)(raw.y >> 16))};
+            float mx = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
             for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-            int e;
             (void)frexpf(mx, &e);
-#pragma unroll
-            for (int k = 0; k < 4; ++k) sm.q[r][l + 64 * k] = ldexpf(v[k], -e);
-            if (l == 0) sm.qe[r] = (float)e;
-        } else {
-#pragma unroll
-            for (int k = 0; k < 4; ++k) sm.q[r][l + 64 * k] = 0.0f;
-            if (l == 0) sm.qe[r] = 0.0f;
         }
+        *reinterpret_cast<f32x4*>(&sm.q[r][4 * l]) =
+            f32x4{ldexpf(v.x, -e), ldexpf(v.y, -e), ldexpf(v.z, -e), ldexpf(v.w, -e)};
+        if (l == 0) sm.qe[r] = (float)e;
     }
     __syncthreads();
 
@@ -244,28 +254,15 @@ __device__ __forceinline__ void int8_split(const Int8Args& a, Int8Smem& sm, int 
     for (int j = 0; j < 16; ++j) O[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
     if (pa < pb) {
-        u32x4 kb[16], vb[16];
+        // One 16-entry register buffer cycles through a page's data: K tiles of
+        // page p are replaced by its V tiles as QK consumes them, and V tiles by
+        // the K tiles of page p+1 as PV consumes them (half a page of lead).
         auto page_base = [&](int p) -> size_t {
             return (size_t)__builtin_amdgcn_readfirstlane(sm.slot[w][p - pa]) * Hkv + kvh;
         };
-        {
-            const size_t base = page_base(pa) * (kP * kD);
-            const int8_t* kp = a.kc + base;
-            const int8_t* vp = a.vc + base;
-#pragma unroll
-            for (int s2 = 0; s2 < 4; ++s2)
-#pragma unroll
-                for (int t = 0; t < 4; ++t) kb[4 * s2 + t] = ld16(kp + koff + (4 * t * kD + 64 * s2));
-#pragma unroll
-            for (int j = 0; j < 16; ++j) vb[j] = ld16(vp + voff + 16 * j * kP);
-            const size_t sb = page_base(pa);
-            const u32x4 sk = ld16(a.kchan + sb * kD + 4 * l);
-            const u32x4 sv = ld16(a.vchan + sb * kD + 4 * l);
-            const float st = a.ktok[sb * kP + l];
-            *reinterpret_cast<u32x4*>(&sm.sc[w][0][4 * l]) = sk;
-            *reinterpret_cast<u32x4*>(&sm.sc[w][0][kD + 4 * l]) = sv;
-            sm.sc[w][0][2 * kD + l] = st * a.scale_log2;
-        }
+        *reinterpret_cast<u32x4*>(&sm.sc[w][0][4 * l]) = sk0;
+        *reinterpret_cast<u32x4*>(&sm.sc[w][0][kD + 4 * l]) = sv0;
+        sm.sc[w][0][2 * kD + l] = st0 * a.scale_log2;
 
         auto page = [&](auto prefetch, int p) {
             constexpr bool PF = decltype(prefetch)::value;
@@ -275,12 +272,11 @@ __device__ __forceinline__ void int8_split(const Int8Args& a, Int8Smem& sm, int 
             u32x4 skn, svn;
             float stn = 0.0f;
             const int8_t* knp = a.kc;
-            const int8_t* vnp = a.vc;
+            const int8_t* vcp = a.vc + page_base(p) * (kP * kD);
             if (PF) {
                 ns = page_base(p + 1);
                 nb = ns * (kP * kD);
                 knp = a.kc + nb;
-                vnp = a.vc + nb;
                 skn = ld16(a.kchan + ns * kD + 4 * l);
                 svn = ld16(a.vchan + ns * kD + 4 * l);
                 stn = a.ktok[ns * kP + l];
@@ -310,15 +306,15 @@ __device__ __forceinline__ void int8_split(const Int8Args& a, Int8Smem& sm, int 
                 }
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
-                    const u32x4 kk = kb[4 * s2 + t];
+                    const u32x4 kk = buf[4 * s2 + t];
                     const half8 a0 = i8x8_to_f16(kk.x, kk.y);
                     const half8 a1 = i8x8_to_f16(kk.z, kk.w);
                     S[t] = mfma_f16(a0, qh[0], S[t]);
                     S[t] = mfma_f16(a0, ql[0], S[t]);
                     S[t] = mfma_f16(a1, qh[1], S[t]);
                     S[t] = mfma_f16(a1, ql[1], S[t]);
-                    if (PF) kb[4 * s2 + t] = ld16(knp + koff + (4 * t * kD + 64 * s2));
-                    __builtin_amdgcn_sched_barrier(0);  // keep conversions next to their MFMAs
+                    buf[4 * s2 + t] = ld16(vcp + voff + 16 * (4 * s2 + t) * kP);  // this page's V tile
+                    // (no scheduling barrier)
                 }
             }
             // logits (base 2): the token factor multiplies the finished dot product
@@ -352,7 +348,7 @@ __device__ __forceinline__ void int8_split(const Int8Args& a, Int8Smem& sm, int 
             // PV on raw value codes; per-channel value scale at the page boundary
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
-                const u32x4 vv = vb[j];
+                const u32x4 vv = buf[j];
                 const half8 a0 = i8x8_to_f16(vv.x, vv.y);
                 const half8 a1 = i8x8_to_f16(vv.z, vv.w);
                 f32x4 c = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -361,8 +357,8 @@ __device__ __forceinline__ void int8_split(const Int8Args& a, Int8Smem& sm, int 
                 const f32x4 vs = *reinterpret_cast<const f32x4*>(&scl[kD + 16 * j + 4 * g]);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) O[j][r] = O[j][r] + vs[r] * c[r];
-                if (PF) vb[j] = ld16(vnp + voff + 16 * j * kP);
-                __builtin_amdgcn_sched_barrier(0);
+                if (PF) buf[j] = ld16(knp + koff + (4 * (j & 3) * kD + 64 * (j >> 2)));  // next page's K tile
+                // (no scheduling barrier)
             }
             if (PF) {
                 float* nsc = sm.sc[w][slot ^ 1];
@@ -541,7 +537,7 @@ union SplitSmem {
     ExactSmem ex;
 };
 
-__global__ __launch_bounds__(kThreads, 1) void decode_int8_kernel(Int8Args a) {
+__global__ __launch_bounds__(kThreads, 2) void decode_int8_kernel(Int8Args a) {
     __shared__ Int8Smem sm;
     int8_split(a, sm, blockIdx.x, blockIdx.y, blockIdx.z);
 }
@@ -551,14 +547,16 @@ __global__ __launch_bounds__(kThreads, 2) void decode_exact_kernel(ExactArgs a) 
     exact_split(a, sm, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
-// Both tiers of a layer in one launch: splits [0, n8) read int8 pages, the
-// rest read the BF16 window; all write partial columns of the same rows.
-__global__ __launch_bounds__(kThreads, 1) void decode_hybrid_kernel(Int8Args a8, ExactArgs ax, int n8) {
+// Both tiers of a layer in one launch: the first nw work-groups of each row
+// read the BF16 window (dispatched first: they are the short ones), the rest
+// read int8 pages; all write partial columns of the same rows (int8 columns
+// first, window columns after them).
+__global__ __launch_bounds__(kThreads, 2) void decode_hybrid_kernel(Int8Args a8, ExactArgs ax, int nw) {
     __shared__ SplitSmem sm;
-    if ((int)blockIdx.x < n8)
-        int8_split(a8, sm.i8, blockIdx.x, blockIdx.y, blockIdx.z);
+    if ((int)blockIdx.x < nw)
+        exact_split(ax, sm.ex, blockIdx.x, blockIdx.y, blockIdx.z);
     else
-        exact_split(ax, sm.ex, blockIdx.x - n8, blockIdx.y, blockIdx.z);
+        int8_split(a8, sm.i8, blockIdx.x - nw, blockIdx.y, blockIdx.z);
 }
 
 static akv_status check_ptrs(const void* const* ptrs, int nptrs) {
@@ -614,6 +612,14 @@ static Int8Args int8_args(const akv_dims* dims, const uint16_t* q, const int8_t*
     return a;
 }
 
+// A wave stages at most kMaxPagesPerWave page slots in LDS.
+static akv_status check_int8_plan(const SplitPlan& p) {
+    if (p.pages_per_split < 1 || p.pages_per_split > 4 * kMaxPagesPerWave)
+        return fail(AKV_ERR_ARG, "int8 pages per work-group %d outside [1, %d]", p.pages_per_split,
+                    4 * kMaxPagesPerWave);
+    return AKV_OK;
+}
+
 static ExactArgs exact_args(const akv_dims* dims, const uint16_t* q, const uint16_t* k_bf16, const uint16_t* v_bf16,
                             const int32_t* page_table, const int32_t* seq_len, int max_pages, float scale,
                             const SplitPlan& plan) {
@@ -652,6 +658,7 @@ extern "C" akv_status akv_decode_attn_int8(const akv_dims* dims, int32_t batch, 
     const int rows = batch * dims->num_kv_heads * dims->group;
     if (max_pages == 0) return akv_fill_empty(rows, dims->head_dim, out_o, out_lse, stream);
     const SplitPlan plan = plan_int8_splits(dims, batch, max_pages);
+    if ((st = check_int8_plan(plan)) != AKV_OK) return st;
     if ((st = check_workspace(workspace, workspace_bytes, partial_bytes(dims, batch, plan.n_splits))) != AKV_OK)
         return st;
     hipStream_t s = (hipStream_t)stream;
@@ -710,8 +717,9 @@ extern "C" akv_status akv_decode_hybrid(const akv_dims* dims, int32_t batch, con
     if ((st = check_ptrs(ptrs, 14)) != AKV_OK) return st;
     const int rows = batch * dims->num_kv_heads * dims->group;
     if (max_pages_int8 + max_pages_window == 0) return akv_fill_empty(rows, dims->head_dim, out_o, out_lse, stream);
-    const SplitPlan p8 = plan_int8_splits(dims, batch, max_pages_int8);
-    const SplitPlan pw = plan_window_splits(dims, batch, max_pages_window);
+    SplitPlan p8, pw;
+    plan_hybrid(dims, batch, max_pages_int8, max_pages_window, &p8, &pw);
+    if (max_pages_int8 > 0 && (st = check_int8_plan(p8)) != AKV_OK) return st;
     const int n_cols = p8.n_splits + pw.n_splits;
     if ((st = check_workspace(workspace, workspace_bytes, partial_bytes(dims, batch, n_cols))) != AKV_OK) return st;
     hipStream_t s = (hipStream_t)stream;
@@ -726,7 +734,7 @@ extern "C" akv_status akv_decode_hybrid(const akv_dims* dims, int32_t batch, con
     ax.part_lse = a8.part_lse;
     dim3 grid((unsigned)n_cols, (unsigned)dims->num_kv_heads, (unsigned)batch);
     prof_begin(s);
-    decode_hybrid_kernel<<<grid, kThreads, 0, s>>>(a8, ax, p8.n_splits);
+    decode_hybrid_kernel<<<grid, kThreads, 0, s>>>(a8, ax, pw.n_splits);
     prof_end(s);
     if ((st = launch_status("decode_hybrid_kernel")) != AKV_OK) return st;
     return launch_combine(rows, dims->head_dim, a8.part_o, a8.part_lse, n_cols, out_o, out_lse, s);
