@@ -3,11 +3,13 @@
     python -m quantized_paged_kv_akv_amd.build
 
 Always recompiles.  The library lands next to this file so it travels with
-the source tree.
+the source tree.  The build fails if any kernel spills registers to scratch
+memory: a spill in the streaming loop costs more than any tuning gains.
 """
 from __future__ import annotations
 
 import os
+import re
 import subprocess
 import sys
 
@@ -26,10 +28,26 @@ FLAGS = [
 ]
 
 
+def resource_usage(text: str) -> dict:
+    """Per-kernel VGPRs, scratch bytes per lane and occupancy from the
+    compiler's kernel-resource-usage remarks."""
+    table, name = {}, None
+    for line in text.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            table[name] = {}
+            continue
+        m = re.search(r"remark:\s+(VGPRs|AGPRs|ScratchSize \[bytes/lane\]|Occupancy \[waves/SIMD\]): (\d+)", line)
+        if m and name:
+            table[name][m.group(1).split(" ")[0]] = int(m.group(2))
+    return table
+
+
 def build(verbose: bool = False) -> str:
     srcs = [os.path.join(HERE, "csrc", s) for s in SOURCES]
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-x", "hip", *srcs, "-o", tmp]
+    cmd = [HIPCC, *FLAGS, "-Rpass-analysis=kernel-resource-usage", "-x", "hip", *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -37,8 +55,17 @@ def build(verbose: bool = False) -> str:
                     if "packed-fp32-ops" not in line)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + out)
-    if verbose and out.strip():
-        print(out)
+    usage = resource_usage(out)
+    spills = {k: v["ScratchSize"] for k, v in usage.items() if v.get("ScratchSize", 0) > 0}
+    if spills:
+        os.remove(tmp)
+        raise RuntimeError(f"kernels spill to scratch (bytes/lane): {spills}")
+    if verbose:
+        rest = "\n".join(line for line in out.splitlines() if "warning:" in line or "error:" in line)
+        if rest.strip():
+            print(rest)
+        for k, v in sorted(usage.items()):
+            print(f"  {k}: {v}")
     os.replace(tmp, LIB)
     return LIB
 

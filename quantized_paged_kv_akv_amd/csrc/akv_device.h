@@ -73,6 +73,12 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
+// The value held by the neighbouring lane of the pair (lanes 2i and 2i+1
+// exchange; a DPP quad permutation [1,0,3,2]).
+__device__ __forceinline__ float swap_pair(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+}
+
 // x = a*b rounded to FP32, split as hi + lo with hi = fp16(x) and
 // lo = fp16(x - hi).  Contraction is off: fusing a*b into the conversions
 // would round hi two different ways and break hi + lo ~ x.

@@ -129,15 +129,19 @@ void plan_hybrid(const akv_dims* d, int batch, int max_pages_int8, int max_pages
     const long long n8 = units * p8->n_splits;
     // A grid a little over one round would leave a few int8 work-groups to run
     // after all the others: widen the int8 work-groups until it fits.
+    // (int8 splits share a request's pages near-equally, so any count works)
     if (n8 + nw > slots && 4 * (n8 + nw) <= 5 * slots && slots - nw >= units) {
-        const int splits = (int)((slots - nw) / units);
+        const int splits = (int)std::min<long long>((slots - nw) / units, max_pages_int8);
         const int q8 = (max_pages_int8 + splits - 1) / splits;
+        // no more work-groups than that many pages each needs: a few slots
+        // stay free, which streams slightly better than a completely full chip
         if ((q8 + 3) / 4 <= kMaxPagesPerWave) *p8 = SplitPlan{q8, (max_pages_int8 + q8 - 1) / q8};
     }
-    if (int v = env_int("AKV_HYBRID_INT8_PAGES")) *p8 = SplitPlan{std::min(v, 4 * kMaxPagesPerWave), 0};
+    if (int v = env_int("AKV_HYBRID_INT8_PAGES")) {
+        const int q8 = std::min(std::min(v, 4 * kMaxPagesPerWave), max_pages_int8);
+        *p8 = SplitPlan{q8, (max_pages_int8 + q8 - 1) / q8};
+    }
     if (int v = env_int("AKV_HYBRID_WINDOW_PAGES")) qw = v;
-    p8->pages_per_split = std::min(p8->pages_per_split, max_pages_int8);
-    p8->n_splits = (max_pages_int8 + p8->pages_per_split - 1) / p8->pages_per_split;
     qw = std::min(qw, max_pages_window);
     *pw = SplitPlan{qw, (max_pages_window + qw - 1) / qw};
 }

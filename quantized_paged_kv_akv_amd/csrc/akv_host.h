@@ -32,9 +32,10 @@ struct SplitPlan {
 };
 SplitPlan plan_splits(const akv_dims* d, int batch, int max_pages);
 
-// Plan of the int8 tier: a work-group owns pages_per_split consecutive pages
-// and splits them near-evenly over its four waves, each of which stages at
-// most kMaxPagesPerWave page slots.
+// Plan of the int8 tier: n_splits work-groups per (request, KV head) share
+// the request's pages near-equally (at most pages_per_split each) and split
+// them near-equally over their four waves, each of which stages at most
+// kMaxPagesPerWave page slots.
 constexpr int kMaxPagesPerWave = 64;
 SplitPlan plan_int8_splits(const akv_dims* d, int batch, int max_pages);
 

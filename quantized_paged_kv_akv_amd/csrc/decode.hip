@@ -51,7 +51,8 @@ struct Int8Args {
     const float* vchan;
     const int32_t* page_table;
     const int32_t* n_pages;
-    int max_pages, Hkv, G, pps;
+    int max_pages, Hkv, G;
+    int splits;        // work-groups per (request, KV head): split s reads pages [s np / splits, (s+1) np / splits)
     int col0, n_cols;  // this tier's first partial column and the partial row stride
     float scale_log2;
     float* part_o;
@@ -163,20 +164,21 @@ __device__ __forceinline__ void write_empty(int G, int Hkv, int kvh, int b, int 
 // computed once.  Per page, lane (n, g) of the wave:
 //   QK   tile t (16 tokens) x channel block s2 (64 channels): the lane's
 //        16-byte load K[16(n>>2) + 4t + (n&3)][64 s2 + 16g .. +16] is the A
-//        operand of two k-steps; the B operand is q' = q (.) c of head n&7 over
-//        the same channels, as an FP16 hi part and lo part (two MFMAs into one
-//        accumulator).  64 MFMAs.
+//        operand of two k-steps; the B operand is q' = q (.) c of head n>>1
+//        over the same channels, its FP16 hi part in even columns and its lo
+//        part in odd ones; a pair of adjacent lanes adds the two results.
+//        32 MFMAs.
 //   softmax over the lane's 16 logits (tokens 16g .. 16g+15) and the group.
 //   PV   channel tile j: the lane's 16-byte load V^T[16j + n][16g .. +16] is
-//        the A operand of two k-steps, P^T the B operand (column n < 8 the hi
-//        part, n >= 8 the lo part).  32 MFMAs.
+//        the A operand of two k-steps, P^T the B operand (hi part of head n>>1
+//        in even columns, lo part in odd ones).  32 MFMAs.
 // The query's FP32 rows sit in LDS; each query row is pre-scaled by a power
 // of two so max|q| < 1, which with max_d c_d >= 1 (the factors multiply to
 // one) keeps every q' inside FP16's range.  The next page's codes are loaded
 // into the registers the current page frees as it consumes them; its scales
-// go to the other half of a per-wave LDS double buffer.  The four waves of a
-// work-group take consecutive page ranges of one (request, KV head) and merge
-// once at the end.
+// go to the other half of a per-wave LDS double buffer.  A work-group owns a
+// near-equal share of one (request, KV head)'s pages; its four waves take
+// every fourth page of it and merge once at the end.
 struct Int8Smem {
     float q[kMaxGroup][kD + 4];    // query rows (scaled by 2^-e per row), FP32; +4 spreads rows over banks
     float qe[kMaxGroup];           // the row's power-of-two exponent e
@@ -189,33 +191,45 @@ struct Int8Smem {
 
 __device__ __forceinline__ void int8_split(const Int8Args& a, Int8Smem& sm, int split, int kvh, int b) {
     const int np = min(a.n_pages[b], a.max_pages);
-    const int wg0 = split * a.pps;  // this work-group's pages [wg0, wg1)
-    if (wg0 >= np) {
+    // this work-group's pages [wg0, wg0 + len): a near-equal share of the request's
+    const int wg0 = (int)((long long)split * np / a.splits);
+    const int len = (int)((long long)(split + 1) * np / a.splits) - wg0;
+    if (len <= 0) {
         write_empty(a.G, a.Hkv, kvh, b, a.n_cols, a.col0 + split, a.part_lse);
         return;
     }
-    const int len = min(np, wg0 + a.pps) - wg0;
     const int tid = threadIdx.x, l = tid & 63, n = l & 15, g = l >> 4;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int G = a.G, Hkv = a.Hkv, Hq = Hkv * G;
-    const int hh = n & 7;
-    const bool lo_lane = n >= 8;
-    // the four waves take near-equal consecutive shares of the range
-    const int pa = wg0 + (w * len) / 4, pb = wg0 + ((w + 1) * len) / 4;
+    // MFMA column n carries head n >> 1: the FP16 hi part in even columns, the
+    // lo part in odd ones (adjacent lanes add them back together)
+    const int hh = n >> 1;
+    const bool lo_lane = (n & 1) != 0;
+    // wave w reads the work-group's pages w, w + 4, w + 8, ...: at any moment
+    // the four waves stream neighbouring pages, which the memory system serves
+    // better than four distant ranges.  The loop runs p = pa .. pb - 1 over
+    // the wave's own page count; page p is table entry pt_index(p - pa).
+    const int cnt = len > w ? (len - w + 3) / 4 : 0;
+    const int pa = wg0 + w, pb = pa + cnt;
+    auto pt_index = [&](int i) { return pa + 4 * i; };
     // per-lane byte offsets inside a page; tile offsets are immediates
     const uint32_t koff = (uint32_t)(qk_row_token(0, n) * kD + 16 * g);
     const uint32_t voff = (uint32_t)(n * kP + 16 * g);
     const int32_t* pt = a.page_table + (size_t)b * a.max_pages;
     const size_t row0 = (size_t)b * Hq + (size_t)kvh * G;
 
-    // The first page's codes and scales are requested before anything else, so
-    // the memory pipeline starts with the work-group; the query staging and the
-    // barrier below overlap their latency.
+    // Requests go out in the order they are needed: this wave's two query
+    // rows, then the first page's codes and scales; the query staging below
+    // waits only for the former and overlaps the latter.
+    const int r0 = w, r1 = w + 4;  // query rows staged by this wave
+    u32x2 qraw0 = {0, 0}, qraw1 = {0, 0};
+    if (r0 < G) qraw0 = *reinterpret_cast<const u32x2*>(a.q + (row0 + r0) * kD + 4 * l);
+    if (r1 < G) qraw1 = *reinterpret_cast<const u32x2*>(a.q + (row0 + r1) * kD + 4 * l);
     u32x4 buf[16];
     u32x4 sk0 = {0, 0, 0, 0}, sv0 = {0, 0, 0, 0};
     float st0 = 0.0f;
-    if (pa < pb) {
-        const size_t sb = (size_t)__builtin_amdgcn_readfirstlane(pt[pa]) * Hkv + kvh;
+    if (cnt > 0) {
+        const size_t sb = (size_t)__builtin_amdgcn_readfirstlane(pt[pt_index(0)]) * Hkv + kvh;
         const int8_t* kp = a.kc + sb * (kP * kD);
 #pragma unroll
         for (int s2 = 0; s2 < 4; ++s2)
@@ -227,25 +241,23 @@ __device__ __forceinline__ void int8_split(const Int8Args& a, Int8Smem& sm, int 
     }
 
     // this wave's page slots, read once (the loop reads them from LDS)
-    for (int i = l; i < pb - pa; i += 64) sm.slot[w][i] = pt[pa + i];
+    for (int i = l; i < cnt; i += 64) sm.slot[w][i] = pt[pt_index(i)];
 
     // query rows of this KV head, FP32, each scaled by 2^-e (e from its max |q|);
     // rows G..7 are zero (the MFMA columns they feed are never read)
-    for (int r = w; r < kMaxGroup; r += 4) {
-        f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+    auto stage_row = [&](int r, u32x2 raw) {
+        f32x4 v = {bf16_to_f32((uint16_t)(raw.x & 0xFFFFu)), bf16_to_f32((uint16_t)(raw.x >> 16)),
+                   bf16_to_f32((uint16_t)(raw.y & 0xFFFFu)), bf16_to_f32((uint16_t)(raw.y >> 16))};
+        float mx = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+        for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
         int e = 0;
-        if (r < G) {
-            const u32x2 raw = *reinterpret_cast<const u32x2*>(a.q + (row0 + r) * kD + 4 * l);
-            v = f32x4{bf16_to_f32((uint16_t)(raw.x & 0xFFFFu)), bf16_to_f32((uint16_t)(raw.x >> 16)),
-                      bf16_to_f32((uint16_t)(raw.y & 0xFFFFu)), bf16_to_f32((uint16_t)(raw.y >> 16))};
-            float mx = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-            for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-            (void)frexpf(mx, &e);
-        }
+        (void)frexpf(mx, &e);
         *reinterpret_cast<f32x4*>(&sm.q[r][4 * l]) =
             f32x4{ldexpf(v.x, -e), ldexpf(v.y, -e), ldexpf(v.z, -e), ldexpf(v.w, -e)};
         if (l == 0) sm.qe[r] = (float)e;
-    }
+    };
+    stage_row(r0, qraw0);  // zero rows stay zero: frexp(0) gives e = 0
+    stage_row(r1, qraw1);
     __syncthreads();
 
     float M = -INFINITY, lsum = 0.0f;
@@ -253,10 +265,11 @@ __device__ __forceinline__ void int8_split(const Int8Args& a, Int8Smem& sm, int 
 #pragma unroll
     for (int j = 0; j < 16; ++j) O[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    if (pa < pb) {
+    if (cnt > 0) {
         // One 16-entry register buffer cycles through a page's data: K tiles of
-        // page p are replaced by its V tiles as QK consumes them, and V tiles by
-        // the K tiles of page p+1 as PV consumes them (half a page of lead).
+        // the wave's page i are replaced by its V tiles as QK consumes them, and
+        // V tiles by the K tiles of page i+1 as PV consumes them (half a page
+        // of lead).
         auto page_base = [&](int p) -> size_t {
             return (size_t)__builtin_amdgcn_readfirstlane(sm.slot[w][p - pa]) * Hkv + kvh;
         };
@@ -289,7 +302,7 @@ __device__ __forceinline__ void int8_split(const Int8Args& a, Int8Smem& sm, int 
             for (int s2 = 0; s2 < 4; ++s2) {
                 const f32x4* qr = reinterpret_cast<const f32x4*>(&sm.q[hh][64 * s2 + 16 * g]);
                 const f32x4* cr = reinterpret_cast<const f32x4*>(&scl[64 * s2 + 16 * g]);
-                half8 qh[2], ql[2];
+                half8 qb[2];  // the hi or the lo part of q', by column
 #pragma unroll
                 for (int i4 = 0; i4 < 4; ++i4) {
                     const f32x4 qq = qr[i4], cc = cr[i4];
@@ -297,26 +310,25 @@ __device__ __forceinline__ void int8_split(const Int8Args& a, Int8Smem& sm, int 
                     for (int e = 0; e < 4; e += 2) {
                         half2 hi, lo;
                         split_prod_f16x2(qq[e], cc[e], qq[e + 1], cc[e + 1], hi, lo);
-                        const int i = 4 * i4 + e;
-                        qh[i >> 3][i & 7] = hi[0];
-                        qh[i >> 3][(i & 7) + 1] = hi[1];
-                        ql[i >> 3][i & 7] = lo[0];
-                        ql[i >> 3][(i & 7) + 1] = lo[1];
+                        const half2 v = lo_lane ? lo : hi;
+                        const int ix = 4 * i4 + e;
+                        qb[ix >> 3][ix & 7] = v[0];
+                        qb[ix >> 3][(ix & 7) + 1] = v[1];
                     }
                 }
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
                     const u32x4 kk = buf[4 * s2 + t];
-                    const half8 a0 = i8x8_to_f16(kk.x, kk.y);
-                    const half8 a1 = i8x8_to_f16(kk.z, kk.w);
-                    S[t] = mfma_f16(a0, qh[0], S[t]);
-                    S[t] = mfma_f16(a0, ql[0], S[t]);
-                    S[t] = mfma_f16(a1, qh[1], S[t]);
-                    S[t] = mfma_f16(a1, ql[1], S[t]);
+                    S[t] = mfma_f16(i8x8_to_f16(kk.x, kk.y), qb[0], S[t]);
+                    S[t] = mfma_f16(i8x8_to_f16(kk.z, kk.w), qb[1], S[t]);
                     buf[4 * s2 + t] = ld16(vcp + voff + 16 * (4 * s2 + t) * kP);  // this page's V tile
-                    // (no scheduling barrier)
                 }
             }
+            // hi + lo: both lanes of a column pair end with the same sum
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) S[t][r] += swap_pair(S[t][r]);
             // logits (base 2): the token factor multiplies the finished dot product
             const float qsc = exp2f(sm.qe[hh]);
             const f32x4* tk = reinterpret_cast<const f32x4*>(&scl[2 * kD + 16 * g]);
@@ -358,7 +370,6 @@ __device__ __forceinline__ void int8_split(const Int8Args& a, Int8Smem& sm, int 
 #pragma unroll
                 for (int r = 0; r < 4; ++r) O[j][r] = O[j][r] + vs[r] * c[r];
                 if (PF) buf[j] = ld16(knp + koff + (4 * (j & 3) * kD + 64 * (j >> 2)));  // next page's K tile
-                // (no scheduling barrier)
             }
             if (PF) {
                 float* nsc = sm.sc[w][slot ^ 1];
@@ -377,7 +388,7 @@ __device__ __forceinline__ void int8_split(const Int8Args& a, Int8Smem& sm, int 
 #pragma unroll
     for (int j = 0; j < 16; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) O[j][r] += __shfl_xor(O[j][r], 8, 64);
+        for (int r = 0; r < 4; ++r) O[j][r] += swap_pair(O[j][r]);
     if (!lo_lane) {
 #pragma unroll
         for (int j = 0; j < 16; ++j)
@@ -604,7 +615,7 @@ static Int8Args int8_args(const akv_dims* dims, const uint16_t* q, const int8_t*
     a.max_pages = max_pages;
     a.Hkv = dims->num_kv_heads;
     a.G = dims->group;
-    a.pps = plan.pages_per_split;
+    a.splits = plan.n_splits;
     a.col0 = 0;
     a.n_cols = plan.n_splits;
     a.scale_log2 = scale * kLog2e;
@@ -612,11 +623,13 @@ static Int8Args int8_args(const akv_dims* dims, const uint16_t* q, const int8_t*
     return a;
 }
 
-// A wave stages at most kMaxPagesPerWave page slots in LDS.
-static akv_status check_int8_plan(const SplitPlan& p) {
-    if (p.pages_per_split < 1 || p.pages_per_split > 4 * kMaxPagesPerWave)
-        return fail(AKV_ERR_ARG, "int8 pages per work-group %d outside [1, %d]", p.pages_per_split,
-                    4 * kMaxPagesPerWave);
+// A wave stages at most kMaxPagesPerWave page slots in LDS: a work-group's
+// share, at most ceil(max_pages / n_splits) pages, must fit four waves.
+static akv_status check_int8_plan(const SplitPlan& p, int max_pages) {
+    const long long per_wg = p.n_splits > 0 ? ((long long)max_pages + p.n_splits - 1) / p.n_splits : 0;
+    if (p.n_splits < 1 || per_wg > 4 * kMaxPagesPerWave)
+        return fail(AKV_ERR_ARG, "int8 split plan of %d splits for %d pages exceeds %d pages per work-group",
+                    p.n_splits, max_pages, 4 * kMaxPagesPerWave);
     return AKV_OK;
 }
 
@@ -658,7 +671,7 @@ extern "C" akv_status akv_decode_attn_int8(const akv_dims* dims, int32_t batch, 
     const int rows = batch * dims->num_kv_heads * dims->group;
     if (max_pages == 0) return akv_fill_empty(rows, dims->head_dim, out_o, out_lse, stream);
     const SplitPlan plan = plan_int8_splits(dims, batch, max_pages);
-    if ((st = check_int8_plan(plan)) != AKV_OK) return st;
+    if ((st = check_int8_plan(plan, max_pages)) != AKV_OK) return st;
     if ((st = check_workspace(workspace, workspace_bytes, partial_bytes(dims, batch, plan.n_splits))) != AKV_OK)
         return st;
     hipStream_t s = (hipStream_t)stream;
@@ -719,7 +732,7 @@ extern "C" akv_status akv_decode_hybrid(const akv_dims* dims, int32_t batch, con
     if (max_pages_int8 + max_pages_window == 0) return akv_fill_empty(rows, dims->head_dim, out_o, out_lse, stream);
     SplitPlan p8, pw;
     plan_hybrid(dims, batch, max_pages_int8, max_pages_window, &p8, &pw);
-    if (max_pages_int8 > 0 && (st = check_int8_plan(p8)) != AKV_OK) return st;
+    if (max_pages_int8 > 0 && (st = check_int8_plan(p8, max_pages_int8)) != AKV_OK) return st;
     const int n_cols = p8.n_splits + pw.n_splits;
     if ((st = check_workspace(workspace, workspace_bytes, partial_bytes(dims, batch, n_cols))) != AKV_OK) return st;
     hipStream_t s = (hipStream_t)stream;
