@@ -239,6 +239,16 @@ class Ring:
         slot = next(t for t in self.slots if t.data_ptr() == addr)
         return slot, offs
 
+    def stage_views(self, layer: int, host_srcs, copy_stream, compute_stream):
+        """Stage `host_srcs` and return device views of the slot, one per
+        source, with its dtype and shape (valid until `release`)."""
+        slot, offs = self.stage(layer, host_srcs, copy_stream, compute_stream)
+        out = []
+        for t, off in zip(host_srcs, offs):
+            nb = t.numel() * t.element_size()
+            out.append(slot[off:off + nb].view(t.dtype).view(t.shape))
+        return out
+
     def release(self, layer: int, compute_stream):
         akv_ring_release(self._h, layer, compute_stream)
 

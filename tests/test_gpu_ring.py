@@ -1,0 +1,144 @@
+"""Host-staged mode through the C ABI: layers staged from pinned host memory
+into a ring of device slots decode bit-identically to the same call on
+HBM-resident copies, including when the ring is reused many times over; an
+oversize layer is refused before any copy, and out-of-order use is refused.
+"""
+import numpy as np
+import pytest
+import torch
+
+from quantized_paged_kv_akv_amd import configs, inputs
+from tests.gpu_util import dev, gpu_quantize, say
+
+pytestmark = pytest.mark.gpu
+SIG = 1.0 / 16.0
+
+
+@pytest.fixture(scope="module")
+def B():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from quantized_paged_kv_akv_amd import binding
+    return binding
+
+
+def _pinned(a: np.ndarray) -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(a)
+    return t.pin_memory()
+
+
+def _layer(B, w, layer):
+    """One layer's hybrid inputs: the int8 pool (codes + scales) and a compact
+    BF16 pool holding only the window pages, as pinned host tensors, plus the
+    query and tables on the device."""
+    d = inputs.make_layer_np(w, layer)
+    plan = d["plan"]
+    src, dst = plan.quant_src_dst()
+    g = gpu_quantize(B, d["k_pool"], d["v_pool"], src, dst, max(1, plan.int8_slots_total), w.num_kv_heads)
+    tw = plan.window_table()
+    kw = d["k_pool"][tw.reshape(-1)]
+    vw = d["v_pool"][tw.reshape(-1)]
+    tw_c = np.arange(tw.size, dtype=np.int32).reshape(tw.shape)
+    srcs = [g[k].cpu().pin_memory() for k in ("k_codes", "v_codes", "k_chan", "k_tok", "v_chan")]
+    srcs += [_pinned(kw), _pinned(vw)]
+    t8 = plan.int8_table()
+    meta = dict(q=dev(d["q"]), t8=dev(t8), n8=dev(np.asarray(plan.n8, np.int32)), m8=t8.shape[1],
+                tw=dev(tw_c), nw=dev(np.asarray(plan.win_tokens, np.int32)), mw=tw.shape[1])
+    return srcs, meta
+
+
+def _decode(B, w, arrs, meta, o, l, ws, stream=None):
+    d8 = B.dims(w.num_kv_heads, w.group)
+    B.akv_decode_hybrid(d8, w.batch, meta["q"], arrs[0], arrs[1], arrs[2], arrs[3], arrs[4], meta["t8"],
+                        meta["n8"], meta["m8"], arrs[5], arrs[6], meta["tw"], meta["nw"], meta["mw"], SIG, o, l,
+                        ws, stream)
+
+
+def _nbytes(srcs):
+    return sum((t.numel() * t.element_size() + 255) // 256 * 256 for t in srcs)
+
+
+def test_ring_staged_equals_resident(B):
+    """Eight layers through a two-slot ring: every slot is reused four times
+    while copies of later layers run on a side stream."""
+    w = configs.tiny()
+    w = inputs.Workload("tiny8", w.cfg_id, batch=w.batch, layers=8, num_kv_heads=w.num_kv_heads, group=w.group,
+                        lengths=w.lengths, window=w.window, outlier_frac=w.outlier_frac, permute=w.permute)
+    layers = [_layer(B, w, i) for i in range(w.layers)]
+    d8 = B.dims(w.num_kv_heads, w.group)
+    m8, mw = layers[0][1]["m8"], layers[0][1]["mw"]
+    ws = torch.empty(max(16, B.akv_decode_hybrid_workspace_bytes(d8, w.batch, m8, mw)), dtype=torch.uint8,
+                     device="cuda")
+    rows = (w.batch, w.num_q_heads)
+    ref = []
+    for srcs, meta in layers:
+        o = torch.empty((*rows, 256), device="cuda")
+        l = torch.empty(rows, device="cuda")
+        _decode(B, w, [t.cuda() for t in srcs], meta, o, l, ws)
+        ref.append((o, l))
+    torch.cuda.synchronize()
+
+    slot_bytes = _nbytes(layers[0][0])
+    say("case ring 8 layers, 2 slots of", slot_bytes, "bytes")
+    slots = [torch.empty(slot_bytes, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    ring = B.Ring(slots)
+    copy_s = torch.cuda.Stream()
+    comp_s = torch.cuda.current_stream()
+    outs = []
+    try:
+        for i, (srcs, meta) in enumerate(layers):
+            views = ring.stage_views(i, srcs, copy_s, comp_s)
+            o = torch.full((*rows, 256), float("nan"), device="cuda")
+            l = torch.full(rows, float("nan"), device="cuda")
+            _decode(B, w, views, meta, o, l, ws, comp_s)
+            ring.release(i, comp_s)
+            outs.append((o, l))
+        torch.cuda.synchronize()
+    finally:
+        ring.destroy()
+    for i, ((o, l), (ro, rl)) in enumerate(zip(outs, ref)):
+        assert torch.equal(o, ro) and torch.equal(l, rl), f"layer {i} differs from the resident decode"
+
+
+def test_ring_refuses_oversize_before_copying(B):
+    w = configs.tiny()
+    srcs, _ = _layer(B, w, 0)
+    need = _nbytes(srcs)
+    slots = [torch.full((need - 256,), 7, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    ring = B.Ring(slots)
+    try:
+        with pytest.raises(B.AkvError) as e:
+            ring.stage(0, srcs, torch.cuda.Stream(), torch.cuda.current_stream())
+        assert e.value.status_name == "AKV_ERR_BUDGET", e.value
+        torch.cuda.synchronize()
+        assert bool((slots[0] == 7).all()) and bool((slots[1] == 7).all()), "a refused stage wrote to a slot"
+    finally:
+        ring.destroy()
+
+
+def test_ring_lifecycle_errors(B):
+    w = configs.tiny()
+    srcs, _ = _layer(B, w, 0)
+    need = _nbytes(srcs)
+    slots = [torch.empty(need, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    ring = B.Ring(slots)
+    cs, ks = torch.cuda.Stream(), torch.cuda.current_stream()
+    try:
+        with pytest.raises(B.AkvError) as e:
+            ring.release(0, ks)  # never staged
+        assert e.value.status_name == "AKV_ERR_STATE"
+        ring.stage(0, srcs, cs, ks)
+        with pytest.raises(B.AkvError) as e:
+            ring.stage(2, srcs, cs, ks)  # same slot (2 % 2), not yet released
+        assert e.value.status_name == "AKV_ERR_STATE"
+        ring.stage(1, srcs, cs, ks)  # the other slot is free
+        ring.release(0, ks)
+        ring.stage(2, srcs, cs, ks)
+        ring.release(1, ks)
+        ring.release(2, ks)
+        torch.cuda.synchronize()
+    finally:
+        ring.destroy()
