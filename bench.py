@@ -36,8 +36,9 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
+    """Hash of the sources that decide the decode kernel's code and launch shape."""
     h = hashlib.sha256()
-    for f in ("decode.hip", "akv_device.h"):
+    for f in ("decode.hip", "akv_device.h", "akv_host.cpp"):
         h.update(open(os.path.join(ROOT, "quantized_paged_kv_akv_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -393,18 +394,24 @@ def profile_kernels(args, w):
 
 
 def load_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel source."""
-    p = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    (profiles/<kernel>_<workload>_counters.md, lines `kernel_source_hash: ...`
+    and `traffic_bytes_per_launch: ...`), if it was taken on the current
+    kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.md")
     if not os.path.exists(p):
         return None
+    fields = {}
+    for line in open(p):
+        if ":" in line and line.split(":", 1)[0].strip() in ("kernel_source_hash", "traffic_bytes_per_launch"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    if fields.get("kernel_source_hash") != kernel_source_hash():
+        return None
     try:
-        t = json.load(open(p))
-    except Exception:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
         return None
-    if t.get("source_hash") != kernel_source_hash():
-        return None
-    return t.get("bytes_per_launch")
 
 
 def main():

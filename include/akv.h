@@ -85,9 +85,10 @@ const char *akv_version(void);
 
 /*
  * Instrumentation (the "ActiveKV" page, "What I built", keeps instrumented
- * runs apart from product timing): on the calling thread, record start_event
- * right before and stop_event right after the split-K kernel of each
- * subsequent decode call (int8, exact or hybrid), on that call's stream.
+ * runs apart from product timing): on the calling thread, the split-K kernel
+ * of each subsequent decode call (int8, exact or hybrid) is launched so that
+ * start_event and stop_event receive that kernel's own start and end
+ * timestamps (hipExtLaunchKernelGGL); the events must allow timing.
  * Both hipEvent_t handles are owned by the caller; pass NULL, NULL to stop.
  * Errors: AKV_ERR_ARG if exactly one of them is NULL.
  */

@@ -24,12 +24,8 @@ void clear_error() { g_err[0] = '\0'; }
 static thread_local hipEvent_t g_prof_start = nullptr;
 static thread_local hipEvent_t g_prof_stop = nullptr;
 
-void prof_begin(hipStream_t s) {
-    if (g_prof_start) (void)hipEventRecord(g_prof_start, s);
-}
-void prof_end(hipStream_t s) {
-    if (g_prof_stop) (void)hipEventRecord(g_prof_stop, s);
-}
+hipEvent_t prof_start_event() { return g_prof_start; }
+hipEvent_t prof_stop_event() { return g_prof_stop; }
 
 akv_status check_dims(const akv_dims* d) {
     if (!d) return fail(AKV_ERR_ARG, "dims is NULL");

@@ -15,11 +15,12 @@ void clear_error();
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Instrumentation: when the calling thread set a pair of events with
-// akv_set_profile_events, they are recorded on the launch stream right before
-// and right after the split-K kernel of the next decode calls.
-void prof_begin(hipStream_t s);
-void prof_end(hipStream_t s);
+// Instrumentation: the event pair the calling thread set with
+// akv_set_profile_events (both NULL when unset).  The decode entry points
+// launch their split-K kernel with hipExtLaunchKernelGGL when it is set, so
+// the events carry that kernel's own start and end timestamps.
+hipEvent_t prof_start_event();
+hipEvent_t prof_stop_event();
 
 // Shape checks common to every attention/quantize call.
 akv_status check_dims(const akv_dims* d);

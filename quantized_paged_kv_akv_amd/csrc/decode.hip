@@ -40,6 +40,8 @@
 #include "akv_device.h"
 #include "akv_host.h"
 
+#include <hip/hip_ext.h>
+
 namespace akv {
 
 struct Int8Args {
@@ -653,6 +655,17 @@ static ExactArgs exact_args(const akv_dims* dims, const uint16_t* q, const uint1
     return a;
 }
 
+// Launch the split-K kernel; with profile events set, through
+// hipExtLaunchKernelGGL so the events time the kernel itself.
+template <typename... A>
+static void launch_split(void (*kernel)(A...), dim3 grid, hipStream_t s, A... args) {
+    hipEvent_t e0 = prof_start_event(), e1 = prof_stop_event();
+    if (e0 && e1)
+        hipExtLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, s, e0, e1, 0, args...);
+    else
+        kernel<<<grid, kThreads, 0, s>>>(args...);
+}
+
 }  // namespace akv
 
 using namespace akv;
@@ -679,9 +692,7 @@ extern "C" akv_status akv_decode_attn_int8(const akv_dims* dims, int32_t batch, 
                            softmax_scale, plan);
     split_workspace(dims, batch, plan.n_splits, workspace, &a.part_o, &a.part_lse);
     dim3 grid((unsigned)plan.n_splits, (unsigned)dims->num_kv_heads, (unsigned)batch);
-    prof_begin(s);
-    decode_int8_kernel<<<grid, kThreads, 0, s>>>(a);
-    prof_end(s);
+    launch_split(decode_int8_kernel, grid, s, a);
     if ((st = launch_status("decode_int8_kernel")) != AKV_OK) return st;
     return launch_combine(rows, dims->head_dim, a.part_o, a.part_lse, plan.n_splits, out_o, out_lse, s);
 }
@@ -705,9 +716,7 @@ extern "C" akv_status akv_decode_attn_exact(const akv_dims* dims, int32_t batch,
     ExactArgs a = exact_args(dims, q, k_bf16, v_bf16, page_table, seq_len, max_pages, softmax_scale, plan);
     split_workspace(dims, batch, plan.n_splits, workspace, &a.part_o, &a.part_lse);
     dim3 grid((unsigned)plan.n_splits, (unsigned)dims->num_kv_heads, (unsigned)batch);
-    prof_begin(s);
-    decode_exact_kernel<<<grid, kThreads, 0, s>>>(a);
-    prof_end(s);
+    launch_split(decode_exact_kernel, grid, s, a);
     if ((st = launch_status("decode_exact_kernel")) != AKV_OK) return st;
     return launch_combine(rows, dims->head_dim, a.part_o, a.part_lse, plan.n_splits, out_o, out_lse, s);
 }
@@ -746,9 +755,7 @@ extern "C" akv_status akv_decode_hybrid(const akv_dims* dims, int32_t batch, con
     ax.part_o = a8.part_o;
     ax.part_lse = a8.part_lse;
     dim3 grid((unsigned)n_cols, (unsigned)dims->num_kv_heads, (unsigned)batch);
-    prof_begin(s);
-    decode_hybrid_kernel<<<grid, kThreads, 0, s>>>(a8, ax, pw.n_splits);
-    prof_end(s);
+    launch_split(decode_hybrid_kernel, grid, s, a8, ax, pw.n_splits);
     if ((st = launch_status("decode_hybrid_kernel")) != AKV_OK) return st;
     return launch_combine(rows, dims->head_dim, a8.part_o, a8.part_lse, n_cols, out_o, out_lse, s);
 }
