@@ -86,9 +86,10 @@ const char *akv_version(void);
 /*
  * Instrumentation (the "ActiveKV" page, "What I built", keeps instrumented
  * runs apart from product timing): on the calling thread, the split-K kernel
- * of each subsequent decode call (int8, exact or hybrid) is launched so that
- * start_event and stop_event receive that kernel's own start and end
- * timestamps (hipExtLaunchKernelGGL); the events must allow timing.
+ * of each subsequent decode call (int8, exact or hybrid) is launched with
+ * start_event and stop_event attached to its dispatch (hipExtLaunchKernelGGL),
+ * so the pair brackets that kernel and its dispatch; the events must allow
+ * timing.
  * Both hipEvent_t handles are owned by the caller; pass NULL, NULL to stop.
  * Errors: AKV_ERR_ARG if exactly one of them is NULL.
  */

@@ -18,7 +18,7 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 // Instrumentation: the event pair the calling thread set with
 // akv_set_profile_events (both NULL when unset).  The decode entry points
 // launch their split-K kernel with hipExtLaunchKernelGGL when it is set, so
-// the events carry that kernel's own start and end timestamps.
+// the events bracket that kernel's dispatch and execution.
 hipEvent_t prof_start_event();
 hipEvent_t prof_stop_event();
 
