@@ -131,11 +131,71 @@ __global__ __launch_bounds__(256) void combine_kernel(int D, int n_splits, const
     if (chunk == 0 && tid == 0) out_lse[r] = m + logf(sum);
 }
 
+// The same pass for up to 8*K splits with every load issued up front: each
+// thread holds the LSE and one channel's O of its K splits in registers, so
+// the whole pass waits on memory once (the loop above waits once per group
+// of four splits, which dominates at the usual hundred-odd splits).
+template <int K>
+__global__ __launch_bounds__(256) void combine_reg_kernel(int D, int n_splits, const float* __restrict__ part_o,
+                                                          const float* __restrict__ part_lse,
+                                                          float* __restrict__ out_o, float* __restrict__ out_lse) {
+    const int r = blockIdx.x, chunk = blockIdx.y;
+    const int tid = threadIdx.x, sl = tid >> 5, c = tid & 31;
+    const int d = chunk * 32 + c;
+    __shared__ float red_m[8], red_w[8], acc_s[8][32];
+    const float* lse = part_lse + (size_t)r * n_splits;
+    const float* po = part_o + (size_t)r * n_splits * D + d;
+    float l[K], o[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const int sp = sl + 8 * k;
+        l[k] = sp < n_splits ? lse[sp] : -INFINITY;
+        o[k] = sp < n_splits ? po[(size_t)sp * D] : 0.0f;
+    }
+    float m = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < K; ++k) m = fmaxf(m, l[k]);
+    if (c == 0) red_m[sl] = m;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 8; ++k) m = fmaxf(m, red_m[k]);
+    if (m == -INFINITY) {  // every split empty
+        if (sl == 0) out_o[(size_t)r * D + d] = 0.0f;
+        if (chunk == 0 && tid == 0) out_lse[r] = -INFINITY;
+        return;
+    }
+    float w = 0.0f, acc = 0.0f;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const float e = (l[k] == -INFINITY) ? 0.0f : expf(l[k] - m);
+        w += e;
+        if (e != 0.0f) acc += e * o[k];  // an empty split's O slot may hold anything
+    }
+    acc_s[sl][c] = acc;
+    if (c == 0) red_w[sl] = w;
+    __syncthreads();
+    if (sl == 0) {
+        float t = 0.0f, W = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            t += acc_s[k][c];
+            W += red_w[k];
+        }
+        out_o[(size_t)r * D + d] = t / W;
+        if (chunk == 0 && c == 0) out_lse[r] = m + logf(W);
+    }
+}
+
 akv_status launch_combine(int rows, int D, const float* part_o, const float* part_lse, int n_splits, float* out_o,
                           float* out_lse, hipStream_t stream) {
     if (rows == 0) return AKV_OK;
     dim3 grid((unsigned)rows, (unsigned)(D / 32));
-    combine_kernel<<<grid, 256, 0, stream>>>(D, n_splits, part_o, part_lse, out_o, out_lse);
+    if (n_splits <= 8 * 16)
+        combine_reg_kernel<16><<<grid, 256, 0, stream>>>(D, n_splits, part_o, part_lse, out_o, out_lse);
+    else if (n_splits <= 8 * 32)
+        combine_reg_kernel<32><<<grid, 256, 0, stream>>>(D, n_splits, part_o, part_lse, out_o, out_lse);
+    else
+        combine_kernel<<<grid, 256, 0, stream>>>(D, n_splits, part_o, part_lse, out_o, out_lse);
     return launch_status("combine_kernel");
 }
 

@@ -201,6 +201,24 @@ def test_exact_decode_parity(B, Hkv, G, seq_len):
     check_attn(o, lse, ro, rl, f"exact Hkv{Hkv} G{G}")
 
 
+@pytest.mark.parametrize("n_pages", [100, 200, 300])
+def test_split_combine_paths(B, monkeypatch, n_pages):
+    """One page per split (a launch-shape override) so the split-K second pass
+    folds 100, 200 and 300 partials per row: its register paths (up to 128
+    and 256 splits) and its looping path; the last page is partial and one
+    request is empty."""
+    monkeypatch.setenv("AKV_PAGES_PER_SPLIT", "1")
+    seq_len = [64 * n_pages - 17, 0]
+    say(f"case split combine n_pages={n_pages}")
+    kp, vp = inputs.random_pools(500 + n_pages, n_pages, 1)
+    table = np.zeros((2, n_pages), np.int32)
+    table[0] = np.random.default_rng(n_pages).permutation(n_pages)
+    q = inputs.random_queries(501, 2, 4)
+    o, lse = run_exact(B, 1, 4, q, dev(kp), dev(vp), table, seq_len)
+    ro, rl = O.decode_exact(q, kp, vp, table, np.asarray(seq_len, np.int32), 1, 4, SIG)
+    check_attn(o, lse, ro, rl, f"combine {n_pages} splits")
+
+
 def test_exact_partial_page_ignores_garbage(B):
     """Tokens past seq_len in the last page may hold anything (here NaN and
     Inf bit patterns); they must not reach the result."""
