@@ -70,10 +70,15 @@ class Workload:
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """Round FP32 to BF16 bits, nearest even (NaN-free inputs)."""
+    """Round FP32 to BF16 bits, nearest even (NaN-free inputs): add 0x7FFF
+    plus the lowest kept bit, keep the high half (in place, one temporary)."""
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
-    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
-    return r.astype(np.uint16)
+    t = np.right_shift(u, np.uint32(16))
+    np.bitwise_and(t, np.uint32(1), out=t)
+    np.add(t, np.uint32(0x7FFF), out=t)
+    np.add(t, u, out=t)
+    np.right_shift(t, np.uint32(16), out=t)
+    return t.astype(np.uint16)
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:

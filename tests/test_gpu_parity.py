@@ -316,3 +316,27 @@ def test_ctx32k_layer_full_size(B):
     src, dst = plan.quant_src_dst()
     sel = np.random.default_rng(0).choice(len(src), 48, replace=False)
     check_quantize(O, d["k_pool"], d["v_pool"], src[sel], dst[sel], plan.int8_slots_total, 4, g, "ctx32k sample")
+
+
+def test_ctx128k_layer_full_size(B):
+    """One full 128K layer (2032 int8 pages + 16 window pages per KV head) in
+    the launch shape the benchmark times: every output row of the int8 tier,
+    the window tier, their merge and the fused hybrid call against the oracle;
+    a sample of pages through the quantizer check."""
+    w = configs.ctx128k()
+    d = inputs.make_layer_np(w, 5)
+    say("case ctx128k layer 5")
+    g = _hybrid_layer(B, w, d, "ctx128k")
+    plan = d["plan"]
+    src, dst = plan.quant_src_dst()
+    sel = np.random.default_rng(1).choice(len(src), 32, replace=False)
+    check_quantize(O, d["k_pool"], d["v_pool"], src[sel], dst[sel], plan.int8_slots_total, 4, g, "ctx128k sample")
+
+
+def test_batched_full_size(B):
+    """All 32 requests of the batched workload (lengths 4K-16K in equal-length
+    pairs, permuted pools, 512-token windows) in one launch per tier."""
+    w = configs.batched()
+    d = inputs.make_layer_np(w, 1)
+    say("case batched 32 requests, layer 1")
+    _hybrid_layer(B, w, d, "batched32")
