@@ -59,14 +59,15 @@ SplitPlan plan_splits(const akv_dims* d, int batch, int max_pages) {
 }
 
 // Two waves per SIMD are resident (2048 on the chip); give each about an equal
-// share of the page-heads, at least 2 pages so the per-wave set-up and the
-// end-of-split merge stay small.  A work-group is four waves, so it owns four
+// share of the page-heads, at least 3 pages so the per-wave set-up, the first
+// page's latency and the end-of-split merge stay small (measured at 32K: 3
+// pages per wave beat 2 by a fifth).  A work-group is four waves, so it owns four
 // waves' worth of consecutive pages.  AKV_PAGES_PER_WAVE overrides (sweeps).
 SplitPlan plan_int8_splits(const akv_dims* d, int batch, int max_pages) {
     SplitPlan p{1, 0};
     if (batch <= 0 || max_pages <= 0) return p;
     long long units = (long long)batch * d->num_kv_heads * max_pages;
-    int ppw = (int)std::max<long long>(2, (units + 2047) / 2048);
+    int ppw = (int)std::max<long long>(3, (units + 2047) / 2048);
     if (const char* e = getenv("AKV_PAGES_PER_WAVE")) {
         int v = atoi(e);
         if (v > 0) ppw = v;
@@ -118,9 +119,10 @@ void plan_hybrid(const akv_dims* d, int batch, int max_pages_int8, int max_pages
     if (batch <= 0 || max_pages_window <= 0 || max_pages_int8 <= 0) return;
     const long long units = (long long)batch * d->num_kv_heads;
     const long long slots = 2LL * device_cu_count();
-    // A BF16 page is twice the bytes of an int8 page: a window work-group of
-    // half as many pages streams as long as an int8 one.
-    int qw = std::max(1, std::min(p8->pages_per_split / 2, max_pages_window));
+    // A BF16 page is twice the bytes of an int8 page, and the exact body
+    // streams more slowly per work-group (a barrier per page): window
+    // work-groups of a quarter as many pages finish with the int8 ones.
+    int qw = std::max(1, std::min(p8->pages_per_split / 4, max_pages_window));
     const long long nw = units * ((max_pages_window + qw - 1) / qw);
     const long long n8 = units * p8->n_splits;
     // A grid a little over one round would leave a few int8 work-groups to run
