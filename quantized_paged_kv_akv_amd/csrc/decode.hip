@@ -401,23 +401,29 @@ __device__ __forceinline__ void int8_split(const Int8Args& a, Int8Smem& sm, int 
         }
     }
     __syncthreads();
-    const int d = tid;  // one thread per channel
-    for (int h = 0; h < G; ++h) {
-        float Ms = -INFINITY;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) Ms = fmaxf(Ms, sm.mm[k][h]);
-        float lt = 0.0f, ot = 0.0f;
+    // item (h, 4 channels) per thread: a wave covers one head, so the per-wave
+    // statistics are broadcast reads and the O reads and stores are 16 bytes
+    for (int it = tid; it < G * (kD / 4); it += kThreads) {
+        const int h = it / (kD / 4), c4 = 4 * (it % (kD / 4));
+        float mk[4], Ms = -INFINITY;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const float mk = sm.mm[k][h];
-            if (mk == -INFINITY) continue;
-            const float f = exp2f(mk - Ms);
+            mk[k] = sm.mm[k][h];
+            Ms = fmaxf(Ms, mk[k]);
+        }
+        float lt = 0.0f;
+        f32x4 ot = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if (mk[k] == -INFINITY) continue;
+            const float f = exp2f(mk[k] - Ms);
             lt += f * sm.ml[k][h];
-            ot += f * sm.mo[k][h][d];
+            ot += f * *reinterpret_cast<const f32x4*>(&sm.mo[k][h][c4]);
         }
         const size_t row = row0 + h;
-        a.part_o[(row * a.n_cols + a.col0 + split) * kD + d] = ot / lt;
-        if (d == 0) a.part_lse[row * a.n_cols + a.col0 + split] = (Ms + log2f(lt)) * kLn2;
+        const float inv = 1.0f / lt;
+        *reinterpret_cast<f32x4*>(&a.part_o[(row * a.n_cols + a.col0 + split) * kD + c4]) = ot * inv;
+        if (c4 == 0) a.part_lse[row * a.n_cols + a.col0 + split] = (Ms + log2f(lt)) * kLn2;
     }
 }
 
