@@ -9,7 +9,9 @@
 //   s_t    = max_d(|K[t][d]| / c_d) / 127                     -> FP32
 //   vs_d   = max_t |V[t][d]| / 127                            -> FP32
 //   codes  = clamp(rint(x / scale), -127, 127) with the quotient an IEEE
-//            float64 divide by the exact product of the FP32 scales.
+//            float64 divide by the exact product of the FP32 scales (taken
+//            only near rounding boundaries; elsewhere a reciprocal product
+//            gives the same integer).
 // The factor normalisation happens before the clamp (the order the format
 // states).  Codes are written in the pool layouts: K token-major, V
 // channel-major.  The kernel reads 64 KB and writes 35,072 B per page-head;
@@ -21,9 +23,23 @@
 
 namespace akv {
 
-__device__ __forceinline__ int code_of(double x, double scale) {
-    if (scale == 0.0) return 0;
-    double r = rint(x / scale);  // round half to even
+// Code of x at scale = a * b (a, b FP32, so the product is exact in float64):
+// round half to even of the float64 quotient x / scale, clamped to +-127.  The
+// quotient is first estimated as x * inv_ab with inv_ab a product of rounded
+// reciprocals (a few ulp off, under 2^-40 absolute for |q| <= 128); only when
+// that estimate lies within 2^-30 of a half-integer (the boundaries of
+// rounding to an integer) is the correctly rounded divide taken, so the
+// result is always that of the IEEE float64 divide.
+__device__ __forceinline__ int code_of(double x, double a, double b, double inv_ab) {
+    if (a * b == 0.0) return 0;
+    const double q = x * inv_ab;
+    const double fl = floor(q);
+    const double fr = q - fl;
+    double r;
+    if (fabs(fr - 0.5) < 0x1p-30)
+        r = rint(x / (a * b));  // near a boundary: the exact quotient decides
+    else
+        r = fr < 0.5 ? fl : fl + 1.0;
     r = fmin(fmax(r, -127.0), 127.0);
     return (int)r;
 }
@@ -41,10 +57,26 @@ __global__ __launch_bounds__(256) void quantize_kernel(
 
     __shared__ uint16_t Ks[kP][kD];
     __shared__ float c32s[kD];
+    __shared__ double invc[kD];
     __shared__ float s32s[kP];
+    __shared__ double invs[kP];
     __shared__ double red_sum[4];
     __shared__ int red_cnt[4];
 
+    // value rows first (thread d owns channel row d: 64 contiguous tokens), so
+    // their latency overlaps the key staging
+    uint32_t vw[32];
+    {
+        const u32x4* row = reinterpret_cast<const u32x4*>(V + (size_t)tid * kP);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const u32x4 x = row[k];
+            vw[4 * k + 0] = x.x;
+            vw[4 * k + 1] = x.y;
+            vw[4 * k + 2] = x.z;
+            vw[4 * k + 3] = x.w;
+        }
+    }
     // stage the key page (32 KB) in LDS with coalesced 16-byte loads
     {
         const u32x4* src4 = reinterpret_cast<const u32x4*>(K);
@@ -82,23 +114,27 @@ __global__ __launch_bounds__(256) void quantize_kernel(
     if (nz) c = fmin(fmax(u / gmean, 1.0 / 16384.0), 16384.0);
     const float c32 = (float)c;
     c32s[d] = c32;
+    invc[d] = 1.0 / (double)c32;
     kchan[dp * kD + d] = c32;
     __syncthreads();
 
-    // token factor: 4 threads per token, 64 channels each
+    // token factor: 4 threads per token, 64 channels each (visited from a
+    // per-token offset so the four-byte LDS words spread over the banks);
+    // the max of |K| / c is taken on |K| * (1/c), which moves s_t by at most
+    // a few float64 ulp before its FP32 rounding
     {
         const int t = tid >> 2, part = tid & 3;
         double m = 0.0;
         for (int e = 0; e < 64; ++e) {
-            const int dd = part * 64 + e;
-            const double a = fabs((double)bf16_to_f32(Ks[t][dd])) / (double)c32s[dd];
-            m = fmax(m, a);
+            const int dd = part * 64 + ((e + 2 * t) & 63);
+            m = fmax(m, fabs((double)bf16_to_f32(Ks[t][dd])) * invc[dd]);
         }
         m = fmax(m, __shfl_xor(m, 1, 64));
         m = fmax(m, __shfl_xor(m, 2, 64));
         const float s32 = (float)(m / 127.0);
         if (part == 0) {
             s32s[t] = s32;
+            invs[t] = s32 != 0.0f ? 1.0 / (double)s32 : 0.0;
             ktok[dp * kP + t] = s32;
         }
     }
@@ -107,25 +143,15 @@ __global__ __launch_bounds__(256) void quantize_kernel(
     // key codes, token-major: thread d writes column d of every token row
     {
         int8_t* out = kcodes + dp * (kP * kD);
-        const double cd = (double)c32s[d];
+        const double cd = (double)c32s[d], icd = invc[d];
         for (int t = 0; t < kP; ++t) {
             const double x = (double)bf16_to_f32(Ks[t][d]);
-            out[t * kD + d] = (int8_t)code_of(x, cd * (double)s32s[t]);
+            out[t * kD + d] = (int8_t)code_of(x, cd, (double)s32s[t], icd * invs[t]);
         }
     }
 
-    // value scale and codes: thread d owns channel row d (64 contiguous tokens)
+    // value scale and codes: channel-major rows of 64 tokens, 16-byte stores
     {
-        const u32x4* row = reinterpret_cast<const u32x4*>(V + (size_t)d * kP);
-        uint32_t vw[32];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            u32x4 x = row[k];
-            vw[4 * k + 0] = x.x;
-            vw[4 * k + 1] = x.y;
-            vw[4 * k + 2] = x.z;
-            vw[4 * k + 3] = x.w;
-        }
         double m = 0.0;
 #pragma unroll
         for (int k = 0; k < 32; ++k) {
@@ -134,7 +160,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(
         }
         const float vs32 = (float)(m / 127.0);
         vchan[dp * kD + d] = vs32;
-        const double vs = (double)vs32;
+        const double vs = (double)vs32, ivs = vs != 0.0 ? 1.0 / vs : 0.0;
         u32x4* out = reinterpret_cast<u32x4*>(vcodes + dp * (kP * kD) + (size_t)d * kP);
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -146,7 +172,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(
                 for (int e = 0; e < 4; ++e) {
                     const int tok = 16 * k + 4 * j + e;
                     const uint16_t b = (tok & 1) ? (uint16_t)(vw[tok >> 1] >> 16) : (uint16_t)(vw[tok >> 1] & 0xFFFFu);
-                    const int cv = code_of((double)bf16_to_f32(b), vs);
+                    const int cv = code_of((double)bf16_to_f32(b), vs, 1.0, ivs);
                     packed |= ((uint32_t)(cv & 0xFF)) << (8 * e);
                 }
                 wds[j] = packed;
