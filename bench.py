@@ -194,6 +194,25 @@ def run_gpu(args, w):
     log("[bench] hybrid step (fused entry) warmup + timed")
     ms_hybrid = timed(hybrid_step, args.steps, args.warmup)
     hyb_us = split_kernel_us(hybrid_step, max(2, args.steps // 2))
+    owners = {}
+    if batch > 1:
+        # the same step as launches of two requests (pairs with equal page
+        # counts, the two-owner form) and as one launch per request
+        wsp = torch.empty(max(16, B.akv_decode_hybrid_workspace_bytes(dims, 2, m8, mw)), dtype=torch.uint8,
+                          device=device)
+
+        def rows_step(k):
+            def step():
+                for i, L in enumerate(layers):
+                    for b0 in range(0, batch, k):
+                        B.akv_decode_hybrid(dims, k, L["q"][b0:b0 + k], L["k_codes"], L["v_codes"], L["k_chan"],
+                                            L["k_tok"], L["v_chan"], T["t8"][b0:b0 + k], T["n8"][b0:b0 + k], m8,
+                                            L["k_pool"], L["v_pool"], T["tw"][b0:b0 + k], T["nw"][b0:b0 + k], mw,
+                                            sigma, out[i][b0:b0 + k], outl[i][b0:b0 + k], wsp, stream)
+            return step
+        log("[bench] two-owner and one-row steps")
+        owners = dict(ms_pairs=timed(rows_step(2), max(2, args.steps // 4), 1),
+                      ms_single=timed(rows_step(1), max(2, args.steps // 4), 1))
     log("[bench] four-call step")
     ms_four = timed(four_call_step, max(2, args.steps // 2), 1)
     log("[bench] all-BF16 step")
@@ -206,7 +225,7 @@ def run_gpu(args, w):
     bf16_bytes = by["bf16_all"] * w.layers
     quant_ms = sum(qt_ms[1:]) / max(1, len(qt_ms) - 1) if len(qt_ms) > 1 else qt_ms[0]
     quant_bytes = n_quant * Hkv * (PAGE_BF16_BYTES + PAGE_INT8_BYTES)
-    return dict(ms_hybrid=ms_hybrid, ms_four=ms_four, ms_bf16=ms_bf16, hybrid_bytes=hybrid_bytes,
+    return dict(owners=owners, ms_hybrid=ms_hybrid, ms_four=ms_four, ms_bf16=ms_bf16, hybrid_bytes=hybrid_bytes,
                 bf16_bytes=bf16_bytes, hyb_launch_us=hyb_us, hyb_bytes_per_launch=layer_bytes,
                 hyb_achieved_gbps=layer_bytes / (hyb_us * 1e-6) / 1e9,
                 bf16_launch_us=bf16_us, bf16_achieved_gbps=by["bf16_all"] / (bf16_us * 1e-6) / 1e9,
@@ -498,6 +517,9 @@ def main():
             "quantize_GBps_read_plus_write": round(r["quant_gbps"], 1),
         },
     }
+    if r["owners"]:
+        res["extra"]["us_per_step_two_owner_launches"] = round(r["owners"]["ms_pairs"] * 1e3, 2)
+        res["extra"]["us_per_step_one_row_launches"] = round(r["owners"]["ms_single"] * 1e3, 2)
     if not args.no_cpu_baseline:
         cb = cpu_baseline(w)
         res["cpu_baseline"] = {k: (round(v, 1) if isinstance(v, float) else v) for k, v in cb.items()}

@@ -23,7 +23,9 @@
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the
  *     default stream).  The return value reports host-side argument checks
  *     and launch errors only; device faults surface at the caller's sync.
- *   - Pointers to tensors must be 16-byte aligned (AKV_ERR_ALIGN otherwise).
+ *   - Pointers to tensors must be 16-byte aligned (AKV_ERR_ALIGN otherwise);
+ *     int32 page tables and length arrays need only 4-byte alignment, so a
+ *     slice of requests' rows can be passed.
  *   - No C++ exception crosses this interface.  akv_last_error() gives a
  *     thread-local message for the last failing call.
  *

@@ -578,10 +578,18 @@ __global__ __launch_bounds__(kThreads, 2) void decode_hybrid_kernel(Int8Args a8,
         int8_split(a8, sm.i8, blockIdx.x - nw, blockIdx.y, blockIdx.z);
 }
 
-static akv_status check_ptrs(const void* const* ptrs, int nptrs) {
+// Tensors: non-NULL and 16-byte aligned.  int32 page tables and length
+// arrays (read one element at a time) need only 4-byte alignment, so a
+// caller can pass a slice of requests.
+static akv_status check_ptrs(const void* const* ptrs, int nptrs, const void* const* tables, int ntables) {
     for (int i = 0; i < nptrs; ++i) {
-        if (!ptrs[i]) return fail(AKV_ERR_ARG, "NULL pointer (argument %d)", i);
-        if (!aligned16(ptrs[i])) return fail(AKV_ERR_ALIGN, "pointer argument %d not 16-byte aligned", i);
+        if (!ptrs[i]) return fail(AKV_ERR_ARG, "NULL pointer (tensor argument %d)", i);
+        if (!aligned16(ptrs[i])) return fail(AKV_ERR_ALIGN, "tensor argument %d not 16-byte aligned", i);
+    }
+    for (int i = 0; i < ntables; ++i) {
+        if (!tables[i]) return fail(AKV_ERR_ARG, "NULL pointer (table argument %d)", i);
+        if ((reinterpret_cast<uintptr_t>(tables[i]) & 3u) != 0)
+            return fail(AKV_ERR_ALIGN, "table argument %d not 4-byte aligned", i);
     }
     return AKV_OK;
 }
@@ -685,8 +693,9 @@ extern "C" akv_status akv_decode_attn_int8(const akv_dims* dims, int32_t batch, 
     clear_error();
     akv_status st = check_shape(dims, batch, max_pages);
     if (st != AKV_OK || batch == 0) return st;
-    const void* ptrs[] = {q, k_codes, v_codes, k_chan, k_tok, v_chan, page_table, n_pages, out_o, out_lse};
-    if ((st = check_ptrs(ptrs, 10)) != AKV_OK) return st;
+    const void* ptrs[] = {q, k_codes, v_codes, k_chan, k_tok, v_chan, out_o, out_lse};
+    const void* tabs[] = {page_table, n_pages};
+    if ((st = check_ptrs(ptrs, 8, tabs, 2)) != AKV_OK) return st;
     const int rows = batch * dims->num_kv_heads * dims->group;
     if (max_pages == 0) return akv_fill_empty(rows, dims->head_dim, out_o, out_lse, stream);
     const SplitPlan plan = plan_int8_splits(dims, batch, max_pages);
@@ -711,8 +720,9 @@ extern "C" akv_status akv_decode_attn_exact(const akv_dims* dims, int32_t batch,
     clear_error();
     akv_status st = check_shape(dims, batch, max_pages);
     if (st != AKV_OK || batch == 0) return st;
-    const void* ptrs[] = {q, k_bf16, v_bf16, page_table, seq_len, out_o, out_lse};
-    if ((st = check_ptrs(ptrs, 7)) != AKV_OK) return st;
+    const void* ptrs[] = {q, k_bf16, v_bf16, out_o, out_lse};
+    const void* tabs[] = {page_table, seq_len};
+    if ((st = check_ptrs(ptrs, 5, tabs, 2)) != AKV_OK) return st;
     const int rows = batch * dims->num_kv_heads * dims->group;
     if (max_pages == 0) return akv_fill_empty(rows, dims->head_dim, out_o, out_lse, stream);
     const SplitPlan plan = plan_splits(dims, batch, max_pages);
@@ -740,9 +750,9 @@ extern "C" akv_status akv_decode_hybrid(const akv_dims* dims, int32_t batch, con
     if (st != AKV_OK) return st;
     if (max_pages_window < 0) return fail(AKV_ERR_ARG, "negative max_pages_window");
     if (batch == 0) return AKV_OK;
-    const void* ptrs[] = {q, k_codes, v_codes, k_chan, k_tok, v_chan, page_table_int8, n_pages_int8,
-                          k_bf16, v_bf16, page_table_window, window_len, out_o, out_lse};
-    if ((st = check_ptrs(ptrs, 14)) != AKV_OK) return st;
+    const void* ptrs[] = {q, k_codes, v_codes, k_chan, k_tok, v_chan, k_bf16, v_bf16, out_o, out_lse};
+    const void* tabs[] = {page_table_int8, n_pages_int8, page_table_window, window_len};
+    if ((st = check_ptrs(ptrs, 10, tabs, 4)) != AKV_OK) return st;
     const int rows = batch * dims->num_kv_heads * dims->group;
     if (max_pages_int8 + max_pages_window == 0) return akv_fill_empty(rows, dims->head_dim, out_o, out_lse, stream);
     SplitPlan p8, pw;

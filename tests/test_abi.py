@@ -62,6 +62,14 @@ def test_host_side_validation(B):
     assert st == -4
     st = lib.akv_decode_attn_exact(ctypes.byref(d), 1, p, p, p, p, p, 2032, 0.0625, p, p, p, 16, None)
     assert st == -4
+    # int32 tables need only 4-byte alignment (slices of requests); tensors need 16
+    t4, t2 = ctypes.c_void_p(20), ctypes.c_void_p(18)
+    st = lib.akv_decode_attn_int8(ctypes.byref(d), 1, p, p, p, p, p, p, t4, t4, 2032, 0.0625, p, p, p, 16, None)
+    assert st == -4
+    st = lib.akv_decode_attn_int8(ctypes.byref(d), 1, p, p, p, p, p, p, t2, t4, 2032, 0.0625, p, p, p, 16, None)
+    assert st == -3
+    st = lib.akv_decode_attn_int8(ctypes.byref(d), 1, t4, p, p, p, p, p, t4, t4, 2032, 0.0625, p, p, p, 16, None)
+    assert st == -3
     # ring refuses fewer than 2 slots and NULL slots
     h = ctypes.c_void_p()
     arr = (ctypes.c_void_p * 1)(ctypes.c_void_p(16))
