@@ -219,13 +219,42 @@ def run_gpu(args, w):
     ms_bf16 = timed(bf16_step, max(2, args.steps // 2), 1)
     bf16_us = split_kernel_us(bf16_step, 2)
 
+    # spread of single steps (events around each of a few more steps)
+    step_us = []
+    for _ in range(max(10, args.steps)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        hybrid_step()
+        e1.record(stream)
+        e1.synchronize()
+        step_us.append(e0.elapsed_time(e1) * 1e3)
+    step_us.sort()
+
+    def pct(q):
+        return step_us[min(len(step_us) - 1, int(q * (len(step_us) - 1) + 0.5))]
+
+    # streaming-read ceiling of this GPU: a plain 16-byte-load read of 4 GiB
+    log("[bench] streaming-read ceiling")
+    big = torch.ones(4 << 30, dtype=torch.uint8, device=device)
+    sink = torch.zeros(1, dtype=torch.int32, device=device)
+    B.akv_stream_read(big, sink, stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(5):
+        B.akv_stream_read(big, sink, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    read_gbps = 5 * (big.numel() // 32768 * 32768) / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del big
+
     by = step_kv_bytes(plan, Hkv)
     layer_bytes = by["int8"] + by["window"]
     hybrid_bytes = layer_bytes * w.layers
     bf16_bytes = by["bf16_all"] * w.layers
     quant_ms = sum(qt_ms[1:]) / max(1, len(qt_ms) - 1) if len(qt_ms) > 1 else qt_ms[0]
     quant_bytes = n_quant * Hkv * (PAGE_BF16_BYTES + PAGE_INT8_BYTES)
-    return dict(owners=owners, ms_hybrid=ms_hybrid, ms_four=ms_four, ms_bf16=ms_bf16, hybrid_bytes=hybrid_bytes,
+    return dict(step_p=(pct(0.1), pct(0.5), pct(0.9)), read_gbps=read_gbps, owners=owners, ms_hybrid=ms_hybrid, ms_four=ms_four, ms_bf16=ms_bf16, hybrid_bytes=hybrid_bytes,
                 bf16_bytes=bf16_bytes, hyb_launch_us=hyb_us, hyb_bytes_per_launch=layer_bytes,
                 hyb_achieved_gbps=layer_bytes / (hyb_us * 1e-6) / 1e9,
                 bf16_launch_us=bf16_us, bf16_achieved_gbps=by["bf16_all"] / (bf16_us * 1e-6) / 1e9,
@@ -371,10 +400,19 @@ def cpu_baseline(w):
     per_step_units = w.batch * w.layers * w.num_kv_heads
     us_per_step = wall * 1e6 * per_step_units / units
     threads = min(O.num_threads(), units)
+    cpu = "unknown CPU"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return dict(value=us_per_step, unit="us/decode step", cores=threads, kind="oracle",
                 sample=f"{units} (request, KV head) units of one {w.name} layer "
                        f"({plan.n8[0]} int8 pages + {plan.win_tokens[0]}-token window each), "
-                       f"float64, {wall:.1f}s wall, scaled x{per_step_units / units:g} to one 16-layer step",
+                       f"float64, {wall:.1f}s wall on {threads} threads of {cpu}, "
+                       f"scaled x{per_step_units / units:g} to one 16-layer step",
                 wall_s=wall)
 
 
@@ -506,6 +544,10 @@ def main():
             "us_per_layer_hybrid": round(ms * 1e3 / w.layers, 2),
             "hybrid_kv_bytes_per_step": r["hybrid_bytes"],
             "hybrid_frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
+            "step_us_p10_p50_p90": [round(x, 1) for x in r["step_p"]],
+            "stream_read_ceiling_GBps": round(r["read_gbps"], 1),
+            "kernel_frac_of_stream_ceiling": round(r["hyb_achieved_gbps"] / r["read_gbps"], 4),
+            "step_frac_of_stream_ceiling": round(value / r["read_gbps"], 4),
             "us_per_step_four_call": round(r["ms_four"] * 1e3, 2),
             "us_per_step_bf16_all": round(r["ms_bf16"] * 1e3, 2),
             "bf16_split_kernel_us": round(r["bf16_launch_us"], 2),

@@ -57,6 +57,7 @@ _SIGS = {
                                          _vp, _i32, _f32, _vp, _vp, _vp, _sz, _vp]),
     "akv_merge_lse": (ctypes.c_int, [_i32, _i32, _vp, _vp, _vp, _vp, _vp]),
     "akv_fill_empty": (ctypes.c_int, [_i32, _i32, _vp, _vp, _vp]),
+    "akv_stream_read": (ctypes.c_int, [_vp, _sz, _vp, _vp]),
     "akv_ring_create": (ctypes.c_int, [ctypes.POINTER(_vp), _sz, _i32, ctypes.POINTER(_vp)]),
     "akv_ring_stage": (ctypes.c_int, [_vp, _i32, ctypes.POINTER(_vp), ctypes.POINTER(_sz), _i32, _vp, _vp,
                                       ctypes.POINTER(_vp), ctypes.POINTER(_sz)]),
@@ -191,6 +192,13 @@ def akv_merge_lse(rows: int, head_dim: int, acc_o, acc_lse, part_o, part_lse, st
 def akv_fill_empty(rows: int, head_dim: int, o, lse, stream=None):
     _check("akv_fill_empty", _lib.akv_fill_empty(rows, head_dim, _ptr(o, torch.float32, "o"),
                                                  _ptr(lse, torch.float32, "lse"), _stream(stream)))
+
+
+def akv_stream_read(buf, sink, stream=None):
+    """One streaming read of the device tensor `buf` (instrumentation)."""
+    _check("akv_stream_read", _lib.akv_stream_read(_ptr(buf, (torch.uint8, torch.int8), "buf"),
+                                                   buf.numel() * buf.element_size(),
+                                                   _ptr(sink, torch.int32, "sink"), _stream(stream)))
 
 
 def akv_ring_create(slots: Sequence[torch.Tensor]):
