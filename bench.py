@@ -288,11 +288,26 @@ def run_staged(args, w):
         h.copy_(t)
         return h
 
+    def packed(ts):
+        """One pinned block per layer holding the tensors back to back at
+        256-byte aligned offsets (one large copy instead of several small
+        ones), plus each tensor's (offset, dtype, shape)."""
+        offs, off = [], 0
+        for t in ts:
+            offs.append(off)
+            off += (t.numel() * t.element_size() + 255) // 256 * 256
+        blk = torch.empty(off, dtype=torch.uint8, pin_memory=True)
+        for t, o in zip(ts, offs):
+            n = t.numel() * t.element_size()
+            blk[o:o + n].copy_(t.contiguous().view(-1).view(torch.uint8))
+        return blk, [(o, t.dtype, tuple(t.shape)) for t, o in zip(ts, offs)]
+
     log("[bench] copying the history to pinned host memory")
-    host_h, host_b = [], []
+    host_h, host_b, lay_h = [], [], None
     for L in layers:
-        host_h.append([pinned(L[k]) for k in ("k_codes", "v_codes", "k_chan", "k_tok", "v_chan")]
-                      + [pinned(L["k_pool"][widx]), pinned(L["v_pool"][widx])])
+        blk, lay_h = packed([L[k] for k in ("k_codes", "v_codes", "k_chan", "k_tok", "v_chan")]
+                            + [L["k_pool"][widx], L["v_pool"][widx]])
+        host_h.append([blk])
         host_b.append([pinned(L["k_pool"]), pinned(L["v_pool"])])
         for k in ("k_codes", "v_codes", "k_chan", "k_tok", "v_chan", "k_pool", "v_pool"):
             del L[k]
@@ -302,7 +317,7 @@ def run_staged(args, w):
     def nbytes(srcs):
         return sum((t.numel() * t.element_size() + 255) // 256 * 256 for t in srcs)
 
-    bytes_h = sum(t.numel() * t.element_size() for t in host_h[0]) * w.layers
+    bytes_h = sum(torch.Size(shp).numel() * torch.empty((), dtype=dt).element_size() for _, dt, shp in lay_h) * w.layers
     bytes_b = sum(t.numel() * t.element_size() for t in host_b[0]) * w.layers
     ring_h = B.Ring([torch.empty(nbytes(host_h[0]), dtype=torch.uint8, device=device) for _ in range(2)])
     ring_b = B.Ring([torch.empty(nbytes(host_b[0]), dtype=torch.uint8, device=device) for _ in range(2)])
@@ -316,7 +331,9 @@ def run_staged(args, w):
 
     def hybrid_step():
         for i, L in enumerate(layers):
-            v = ring_h.stage_views(i, host_h[i], copy_s, comp)
+            slot = ring_h.stage_views(i, host_h[i], copy_s, comp)[0]
+            v = [slot[o:o + torch.Size(shp).numel() * torch.empty((), dtype=dt).element_size()].view(dt).view(shp)
+                 for o, dt, shp in lay_h]
             B.akv_decode_hybrid(dims, w.batch, L["q"], v[0], v[1], v[2], v[3], v[4], T["t8"], T["n8"], m8, v[5],
                                 v[6], tw_c, T["nw"], mw, sigma, out, outl, wsh, comp)
             ring_h.release(i, comp)
@@ -363,6 +380,55 @@ def run_staged(args, w):
     ring_h.destroy()
     ring_b.destroy()
     return dict(ms_h=ms_h, ms_b=ms_b, bytes_h=bytes_h, bytes_b=bytes_b, h2d_gbps=h2d_gbps, steps=steps)
+
+
+def pcie_curve(sizes_mib=(0.0625, 0.25, 1, 4, 16, 64, 256, 512)):
+    """Pinned host-to-device copy rate against transfer size (the transfer
+    model of the exact-vs-hybrid gate)."""
+    import torch
+
+    device = torch.device("cuda", 0)
+    out = []
+    big = torch.empty(int(max(sizes_mib) * (1 << 20)), dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(big.numel(), dtype=torch.uint8, device=device)
+    for mib in sizes_mib:
+        n = int(mib * (1 << 20))
+        reps = max(3, min(200, int(256 / max(mib, 1e-3))))
+        dst[:n].copy_(big[:n], non_blocking=True)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            dst[:n].copy_(big[:n], non_blocking=True)
+        e1.record()
+        torch.cuda.synchronize()
+        out.append((mib, reps * n / (e0.elapsed_time(e1) * 1e-3) / 1e9))
+    return out
+
+
+def staged_sweep(args):
+    """Host-staged per-token time against context length, exact (all-BF16)
+    against hybrid, and the tier the measured times choose at each length."""
+    import gc
+
+    import torch
+
+    from quantized_paged_kv_akv_amd import inputs
+
+    rows = []
+    for L in (8192, 16384, 32768, 65536, 131072):
+        w = inputs.Workload(f"staged{L // 1024}k", 4, batch=1, layers=16, num_kv_heads=4, group=6, lengths=(L,),
+                            window=1024, outlier_frac=0.02, permute=False)
+        r = run_staged(args, w)
+        rows.append(dict(context=L, ms_hybrid=round(r["ms_h"], 3), ms_bf16=round(r["ms_b"], 3),
+                         bytes_hybrid=r["bytes_h"], bytes_bf16=r["bytes_b"],
+                         pcie_GBps_hybrid=round(r["bytes_h"] / (r["ms_h"] * 1e-3) / 1e9, 1),
+                         pcie_GBps_bf16=round(r["bytes_b"] / (r["ms_b"] * 1e-3) / 1e9, 1),
+                         chosen="hybrid" if r["ms_h"] < r["ms_b"] else "exact"))
+        log(f"[bench] {w.name}: hybrid {r['ms_h']:.2f} ms, exact {r['ms_b']:.2f} ms")
+        gc.collect()
+        torch.cuda.empty_cache()
+    return rows
 
 
 def cpu_baseline(w):
@@ -487,9 +553,18 @@ def main():
         sys.exit(2)
 
     from quantized_paged_kv_akv_amd import configs
-    w = configs.ALL[args.workload]()
+    w = configs.ALL[args.workload]() if args.workload in configs.ALL else configs.staged128k()
     if args.profile_kernels:
         profile_kernels(args, w)
+        return
+    if args.workload == "staged-sweep":
+        curve = pcie_curve()
+        rows = staged_sweep(args)
+        print(json.dumps({"metric": "host-staged ms/token vs context, exact vs hybrid (the tier gate)",
+                          "unit": "ms/token", "n_gpus": 1, "higher_is_better": False,
+                          "data": "synthetic (the ctx128k recipe at each context length, pinned host history)",
+                          "pcie_h2d_curve_MiB_GBps": [[m, round(g, 2)] for m, g in curve],
+                          "contexts": rows}), flush=True)
         return
     if w.name == "staged128k":
         r = run_staged(args, w)
