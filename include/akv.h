@@ -235,6 +235,42 @@ akv_status akv_merge_lse(int32_t rows, int32_t head_dim, float *acc_o, float *ac
 akv_status akv_fill_empty(int32_t rows, int32_t head_dim, float *o, float *lse, void *stream);
 
 /*
+ * Streaming page publication ("ActiveKV" page, "What I built"): a page leaves
+ * the exact window only once it is full in every layer; its conversion runs
+ * beside decode and never stalls it, and until it is published decode keeps
+ * serving it exact.
+ *
+ * akv_publish_pages: on side_stream, waits for ready_event (if not NULL;
+ *   recorded by the caller on its compute stream once the pages are full),
+ *   converts the n pages exactly as akv_quantize_pages does (same arguments
+ *   and layouts), then records done_event (if not NULL).  Call it once per
+ *   layer (each layer has its own pools); pass done_event on the last call.
+ *   Returns at once.  Errors as akv_quantize_pages, plus AKV_ERR_HIP.
+ * akv_tables_advance: one small kernel on `stream`, to be enqueued after the
+ *   caller has seen done_event complete (hipEventQuery; the host never waits
+ *   for it).  For each request b (device int32 arrays, 4-byte aligned):
+ *   count[b] pages are published -- new_int8[b][0 .. count[b]) (row stride
+ *   max_new) are appended at int8_table[b][n_pages_int8[b] ..] and
+ *   n_pages_int8[b] grows by count[b]; the first count[b] entries of
+ *   window_table[b] are dropped and its other max_pages_window - count[b]
+ *   entries move to the front (slots reserved past the window's current
+ *   pages move with them; the last count[b] entries keep their values), and
+ *   window_len[b] shrinks by 64 * count[b].  A row whose update would not fit
+ *   (count < 0 or > max_new, int8 table full, or fewer than 64 * count
+ *   window tokens) is left unchanged and, if `status` (device int32 [batch])
+ *   is not NULL, flagged -1 there (0 otherwise).  The caller owns all arrays.
+ *   Errors: AKV_ERR_ARG, AKV_ERR_ALIGN, AKV_ERR_HIP.
+ */
+akv_status akv_publish_pages(const akv_dims *dims, int32_t n, const uint16_t *k_bf16, const uint16_t *v_bf16,
+                             const int32_t *src_slot, const int32_t *dst_slot, int8_t *k_codes, int8_t *v_codes,
+                             float *k_chan, float *k_tok, float *v_chan, void *ready_event, void *side_stream,
+                             void *done_event);
+akv_status akv_tables_advance(int32_t batch, const int32_t *count, const int32_t *new_int8, int32_t max_new,
+                              int32_t *int8_table, int32_t *n_pages_int8, int32_t max_pages_int8,
+                              int32_t *window_table, int32_t *window_len, int32_t max_pages_window,
+                              int32_t *status, void *stream);
+
+/*
  * Host-staged mode ("ActiveKV" page, "The idea" and "What I built"): the
  * authoritative history sits in pinned host memory and each step stages one
  * layer at a time into a ring of device slots, with events so a slot is

@@ -58,6 +58,8 @@ _SIGS = {
     "akv_merge_lse": (ctypes.c_int, [_i32, _i32, _vp, _vp, _vp, _vp, _vp]),
     "akv_fill_empty": (ctypes.c_int, [_i32, _i32, _vp, _vp, _vp]),
     "akv_stream_read": (ctypes.c_int, [_vp, _sz, _vp, _vp]),
+    "akv_publish_pages": (ctypes.c_int, [_D, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "akv_tables_advance": (ctypes.c_int, [_i32, _vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp]),
     "akv_ring_create": (ctypes.c_int, [ctypes.POINTER(_vp), _sz, _i32, ctypes.POINTER(_vp)]),
     "akv_ring_stage": (ctypes.c_int, [_vp, _i32, ctypes.POINTER(_vp), ctypes.POINTER(_sz), _i32, _vp, _vp,
                                       ctypes.POINTER(_vp), ctypes.POINTER(_sz)]),
@@ -192,6 +194,32 @@ def akv_merge_lse(rows: int, head_dim: int, acc_o, acc_lse, part_o, part_lse, st
 def akv_fill_empty(rows: int, head_dim: int, o, lse, stream=None):
     _check("akv_fill_empty", _lib.akv_fill_empty(rows, head_dim, _ptr(o, torch.float32, "o"),
                                                  _ptr(lse, torch.float32, "lse"), _stream(stream)))
+
+
+def _event(e) -> _vp:
+    return _vp(e.cuda_event) if e is not None else _vp(0)
+
+
+def akv_publish_pages(d: akv_dims, n: int, k_bf16, v_bf16, src_slot, dst_slot, k_codes, v_codes, k_chan, k_tok,
+                      v_chan, ready_event=None, side_stream=None, done_event=None):
+    """Events are torch.cuda.Event objects already recorded once (so the HIP
+    event exists) or None."""
+    _check("akv_publish_pages", _lib.akv_publish_pages(
+        ctypes.byref(d), n, _ptr(k_bf16, _BF16, "k_bf16"), _ptr(v_bf16, _BF16, "v_bf16"),
+        _ptr(src_slot, torch.int32, "src_slot"), _ptr(dst_slot, torch.int32, "dst_slot"),
+        _ptr(k_codes, torch.int8, "k_codes"), _ptr(v_codes, torch.int8, "v_codes"),
+        _ptr(k_chan, torch.float32, "k_chan"), _ptr(k_tok, torch.float32, "k_tok"),
+        _ptr(v_chan, torch.float32, "v_chan"), _event(ready_event), _stream(side_stream), _event(done_event)))
+
+
+def akv_tables_advance(batch: int, count, new_int8, int8_table, n_pages_int8, window_table, window_len,
+                       status=None, stream=None):
+    _check("akv_tables_advance", _lib.akv_tables_advance(
+        batch, _ptr(count, torch.int32, "count"), _ptr(new_int8, torch.int32, "new_int8"), new_int8.shape[-1],
+        _ptr(int8_table, torch.int32, "int8_table"), _ptr(n_pages_int8, torch.int32, "n_pages_int8"),
+        int8_table.shape[-1], _ptr(window_table, torch.int32, "window_table"),
+        _ptr(window_len, torch.int32, "window_len"), window_table.shape[-1],
+        _ptr(status, torch.int32, "status"), _stream(stream)))
 
 
 def akv_stream_read(buf, sink, stream=None):
