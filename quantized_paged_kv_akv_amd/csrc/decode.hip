@@ -9,20 +9,19 @@
 // Exact tier ("SYCL" page, "A merge that joins the tiers"): BF16 decode that
 // also returns the log-sum-exp, -inf for an empty range.
 //
-// Work decomposition (both kernels).  A work-group of 4 waves owns one
-// (split of pages, KV head, request).  Wave w owns channels [64w, 64w+64):
-//   QK   S^T(tokens x heads) = K Q^T over the wave's channels, 16x16x32
-//        MFMAs with 16 token rows per tile and 4 tiles per page; the four
-//        waves' partial sums meet in LDS once per page (the only barrier).
-//   PV   O^T(channels x heads) = V^T P^T for the wave's 64 channels, with V
-//        read channel-major so a lane's 16-byte load is one MFMA operand.
-// The 16 MFMA columns hold the G query heads twice: columns h and h+8 carry
-// head h, so the FP32 softmax weights P can be fed as a high and a low
-// half-precision part (column h: hi, column h+8: lo) in a single MFMA; the
-// two halves of O are added once at the end.  For the int8 tier the query
-// times channel factor is likewise split hi + lo (two MFMAs into one
-// accumulator), after scaling each column by a power of two so FP16 neither
-// overflows nor loses the small channels.  Int8 codes become FP16 exactly.
+// Both tiers contract with 16x16x32 MFMAs (FP16 for int8 codes, which become
+// FP16 exactly; BF16 for the exact tier), QK as S^T (tokens x heads) = K Q^T
+// and PV as O^T (channels x heads) = V^T P^T, with V stored channel-major so
+// a lane's 16-byte load is one PV operand.  The 16 MFMA columns carry each
+// query head twice, so an FP32 operand (q' for the int8 tier, the softmax
+// weights P for both) is fed as a high and a low half-precision part in one
+// MFMA and the two halves of the result are added afterwards.
+//
+// Work decomposition.  int8 tier: one wave owns whole pages (no barrier per
+// page); a work-group's four waves share a range of one (request, KV head)'s
+// pages and merge once at the end (details above int8_split).  Exact tier: a
+// work-group owns a range of pages and wave w owns channels [64w, 64w+64);
+// the four waves' partial logits meet in LDS once per page.
 //
 // Token order inside a page: A-operand row i of QK tile t is token
 // 16*(i>>2) + 4t + (i&3).  The MFMA result then gives lane group g the tokens
@@ -426,6 +425,16 @@ __device__ __forceinline__ void int8_split(const Int8Args& a, Int8Smem& sm, int 
         if (c4 == 0) a.part_lse[row * a.n_cols + a.col0 + split] = (Ms + log2f(lt)) * kLn2;
     }
 }
+
+// --------------------------------------------------------------- exact tier
+// A work-group owns pages [p0, p1) of one (request, KV head); wave w owns
+// channels [64w, 64w + 64).  Per page: each wave's QK partial logits (its 64
+// channels) go to LDS, one barrier, every wave sums the four and runs the
+// same softmax, and PV runs over the wave's own channels with P fed hi
+// (columns h < 8) and lo (columns h + 8).  The query is exact in BF16 and
+// stays the B operand; the next page's K and V are loaded at the start of
+// the current one; the last, partial page masks logits and zeroes the value
+// elements past the length so padding never reaches the MFMA.
 
 // zero the BF16 elements of an 8-token operand whose token index >= limit
 __device__ __forceinline__ u32x4 mask_tokens(u32x4 v, int first, int limit) {
