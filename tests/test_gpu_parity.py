@@ -152,6 +152,20 @@ def test_int8_decode_parity(B, Hkv, G, n_pages):
     check_attn(o, lse, ro, rl, f"int8 Hkv{Hkv} G{G}")
 
 
+@pytest.mark.parametrize("pages_per_wave", [None, "64"])
+def test_int8_long_context(B, monkeypatch, pages_per_wave):
+    """A 512K-token history (8192 int8 pages) of one KV head: with the default
+    plan, 512 splits (the looping second pass); with 64 pages per wave (the
+    launch-shape override), every wave at the 64 page slots it can stage."""
+    if pages_per_wave:
+        monkeypatch.setenv("AKV_PAGES_PER_WAVE", pages_per_wave)
+    say(f"case int8 long context 8192 pages, pages per wave {pages_per_wave or 'planned'}")
+    g, table, q = _int8_case(B, 808, 1, 4, [8192])
+    o, lse = run_int8(B, 1, 4, q, g, table, [8192])
+    ro, rl = oracle_int8(O, 1, 4, q, g, table, [8192])
+    check_attn(o, lse, ro, rl, "int8 8192 pages")
+
+
 def test_int8_decode_deterministic(B):
     g, table, q = _int8_case(B, 7, 4, 6, [150])
     say("case int8 determinism")

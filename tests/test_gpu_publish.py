@@ -135,3 +135,25 @@ def test_streaming_publication(B):
                               np.stack([rl8.reshape(rows), rlw.reshape(rows)]))
             o, lse = outs[l]
             check_attn(o.view(rows, D), lse.view(rows), rm, rlm, f"step {s} layer {l} n8={n8s} window={wlen}")
+
+
+def test_tables_advance_refuses_rows_that_do_not_fit(B):
+    """Rows whose update would not fit are left unchanged and flagged; the
+    others are updated (one launch, three requests)."""
+    cap = 4
+    t8 = torch.tensor([[0, 1, 0, 0], [5, 6, 7, 0], [2, 0, 0, 0]], dtype=torch.int32, device="cuda")
+    n8 = torch.tensor([2, 3, 1], dtype=torch.int32, device="cuda")
+    tw = torch.tensor([[2, 3, 9, 9], [8, 9, 10, 11], [3, 4, 5, 6]], dtype=torch.int32, device="cuda")
+    wl = torch.tensor([100, 150, 40], dtype=torch.int32, device="cuda")
+    count = torch.tensor([1, 2, 1], dtype=torch.int32, device="cuda")  # row 1: int8 table full; row 2: < 64 tokens
+    new = torch.tensor([[2, 0], [8, 9], [3, 0]], dtype=torch.int32, device="cuda")
+    status = torch.full((3,), 7, dtype=torch.int32, device="cuda")
+    say("case tables advance with refused rows")
+    B.akv_tables_advance(3, count, new, t8, n8, tw, wl, status)
+    torch.cuda.synchronize()
+    assert status.tolist() == [0, -1, -1]
+    assert t8.tolist() == [[0, 1, 2, 0], [5, 6, 7, 0], [2, 0, 0, 0]]
+    assert n8.tolist() == [3, 3, 1]
+    assert tw.tolist() == [[3, 9, 9, 9], [8, 9, 10, 11], [3, 4, 5, 6]]
+    assert wl.tolist() == [36, 150, 40]
+    assert cap == t8.shape[1]
