@@ -39,7 +39,13 @@
  *              V  [slot][Hkv][D][P]   channel-major (a page of values is
  *                                     stored transposed, so each channel's
  *                                     64 tokens are contiguous)
- *   int8 pool  k_codes [slot][Hkv][P][D]   int8, token-major
+ *   int8 pool  k_codes [slot][Hkv][16384] int8 in tile order: code
+ *                      K[t][d] of a page-head sits at byte
+ *                        ((4 (d / 64) + (t / 4) % 4) * 64 + 16 ((d / 16) % 4)
+ *                         + 4 (t / 16) + t % 4) * 16 + d % 16,
+ *                      so the page is 16 tiles of 1 KB, each holding 16
+ *                      whole 64-byte channel runs of 16 tokens in the
+ *                      order the decode kernel consumes them
  *              v_codes [slot][Hkv][D][P]   int8, channel-major
  *              k_chan  [slot][Hkv][D]      FP32 per-channel key factor
  *              k_tok   [slot][Hkv][P]      FP32 per-token key factor

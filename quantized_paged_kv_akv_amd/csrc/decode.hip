@@ -164,8 +164,10 @@ __device__ __forceinline__ void write_empty(int G, int Hkv, int kvh, int b, int 
 // One wave owns whole pages, so a page needs no barrier and its softmax is
 // computed once.  Per page, lane (n, g) of the wave:
 //   QK   tile t (16 tokens) x channel block s2 (64 channels): the lane's
-//        16-byte load K[16(n>>2) + 4t + (n&3)][64 s2 + 16g .. +16] is the A
-//        operand of two k-steps; the B operand is q' = q (.) c of head n>>1
+//        16-byte load K[16(n>>2) + 4t + (n&3)][64 s2 + 16g .. +16] (bytes
+//        [1024 (4 s2 + t) + 16 lane, +16) of the tile-ordered page, so a
+//        load instruction reads 1 KB contiguous) is the A operand of two
+//        k-steps; the B operand is q' = q (.) c of head n>>1
 //        over the same channels, its FP16 hi part in even columns and its lo
 //        part in odd ones; a pair of adjacent lanes adds the two results.
 //        32 MFMAs.
@@ -173,7 +175,8 @@ __device__ __forceinline__ void write_empty(int G, int Hkv, int kvh, int b, int 
 //   PV   channel tile j: the lane's 16-byte load V^T[16j + n][16g .. +16] is
 //        the A operand of two k-steps, P^T the B operand (hi part of head n>>1
 //        in even columns, lo part in odd ones).  32 MFMAs.
-// The query's FP32 rows sit in LDS; each query row is pre-scaled by a power
+// Code tiles stream with the non-temporal hint (each is read once, in whole
+// lines).  The query's FP32 rows sit in LDS; each query row is pre-scaled by a power
 // of two so max|q| < 1, which with max_d c_d >= 1 (the factors multiply to
 // one) keeps every q' inside FP16's range.  The next page's codes are loaded
 // into the registers the current page frees as it consumes them; its scales
@@ -214,7 +217,7 @@ __device__ __forceinline__ void int8_split(const Int8Args& a, Int8Smem& sm, int 
     const int pa = wg0 + w, pb = pa + cnt;
     auto pt_index = [&](int i) { return pa + 4 * i; };
     // per-lane byte offsets inside a page; tile offsets are immediates
-    const uint32_t koff = (uint32_t)(qk_row_token(0, n) * kD + 16 * g);
+    const uint32_t koff = (uint32_t)(16 * l);  // K codes in tile order: tile i is bytes [1024 i, 1024 i + 1024)
     const uint32_t voff = (uint32_t)(n * kP + 16 * g);
     const int32_t* pt = a.page_table + (size_t)b * a.max_pages;
     const size_t row0 = (size_t)b * Hq + (size_t)kvh * G;
@@ -235,7 +238,7 @@ __device__ __forceinline__ void int8_split(const Int8Args& a, Int8Smem& sm, int 
 #pragma unroll
         for (int s2 = 0; s2 < 4; ++s2)
 #pragma unroll
-            for (int t = 0; t < 4; ++t) buf[4 * s2 + t] = ld16(kp + koff + (4 * t * kD + 64 * s2));
+            for (int t = 0; t < 4; ++t) buf[4 * s2 + t] = ld16_stream(kp + koff + 1024 * (4 * s2 + t));
         sk0 = ld16(a.kchan + sb * kD + 4 * l);
         sv0 = ld16(a.vchan + sb * kD + 4 * l);
         st0 = a.ktok[sb * kP + l];
@@ -322,7 +325,7 @@ __device__ __forceinline__ void int8_split(const Int8Args& a, Int8Smem& sm, int 
                     const u32x4 kk = buf[4 * s2 + t];
                     S[t] = mfma_f16(i8x8_to_f16(kk.x, kk.y), qb[0], S[t]);
                     S[t] = mfma_f16(i8x8_to_f16(kk.z, kk.w), qb[1], S[t]);
-                    buf[4 * s2 + t] = ld16(vcp + voff + 16 * (4 * s2 + t) * kP);  // this page's V tile
+                    buf[4 * s2 + t] = ld16_stream(vcp + voff + 16 * (4 * s2 + t) * kP);  // this page's V tile
                 }
             }
             // hi + lo: both lanes of a column pair end with the same sum
@@ -370,7 +373,7 @@ __device__ __forceinline__ void int8_split(const Int8Args& a, Int8Smem& sm, int 
                 const f32x4 vs = *reinterpret_cast<const f32x4*>(&scl[kD + 16 * j + 4 * g]);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) O[j][r] = O[j][r] + vs[r] * c[r];
-                if (PF) buf[j] = ld16(knp + koff + (4 * (j & 3) * kD + 64 * (j >> 2)));  // next page's K tile
+                if (PF) buf[j] = ld16_stream(knp + koff + 1024 * j);  // next page's K tile
             }
             if (PF) {
                 float* nsc = sm.sc[w][slot ^ 1];

@@ -13,7 +13,7 @@
 //            only near rounding boundaries; elsewhere a reciprocal product
 //            gives the same integer).
 // The factor normalisation happens before the clamp (the order the format
-// states).  Codes are written in the pool layouts: K token-major, V
+// states).  Codes are written in the pool layouts: K in tile order, V
 // channel-major.  The kernel reads 64 KB and writes 35,072 B per page-head;
 // it is off the decode path.
 #include <math.h>
@@ -140,13 +140,14 @@ __global__ __launch_bounds__(256) void quantize_kernel(
     }
     __syncthreads();
 
-    // key codes, token-major: thread d writes column d of every token row
+    // key codes in tile order (kcode_offset): thread d writes channel d of
+    // every token; 16 neighbouring channels land in one 16-byte run
     {
         int8_t* out = kcodes + dp * (kP * kD);
         const double cd = (double)c32s[d], icd = invc[d];
         for (int t = 0; t < kP; ++t) {
             const double x = (double)bf16_to_f32(Ks[t][d]);
-            out[t * kD + d] = (int8_t)code_of(x, cd, (double)s32s[t], icd * invs[t]);
+            out[kcode_offset(t, d)] = (int8_t)code_of(x, cd, (double)s32s[t], icd * invs[t]);
         }
     }
 

@@ -22,6 +22,26 @@ def say(*a):
     sys.stdout.flush()
 
 
+def _kcode_order() -> np.ndarray:
+    """Byte offset, inside a page-head's 16 KB of key codes, of K[t][d] for
+    t*256 + d: the tile order include/akv.h states for k_codes."""
+    t = np.arange(64)[:, None]
+    d = np.arange(256)[None, :]
+    tile = 4 * (d // 64) + (t // 4) % 4
+    lane = 16 * ((d // 16) % 4) + 4 * (t // 16) + t % 4
+    return ((tile * 64 + lane) * 16 + d % 16).reshape(-1)
+
+
+KCODE_ORDER = _kcode_order()
+
+
+def k_codes_token_major(a: np.ndarray) -> np.ndarray:
+    """The library's tile-ordered key codes [..., 64, 256] (16 KB per
+    page-head) as token-major K[t][d], the oracle's layout."""
+    flat = np.ascontiguousarray(a).reshape(a.shape[:-2] + (64 * 256,))
+    return flat[..., KCODE_ORDER].reshape(a.shape)
+
+
 def dev(a: np.ndarray) -> torch.Tensor:
     a = np.ascontiguousarray(a)
     if a.dtype == np.uint16:
@@ -67,6 +87,8 @@ def check_quantize(O, kpool, vpool, src, dst, n_out, Hkv, g, tag=""):
     n_ties = 0
     for k, t in (("k_codes", "k_ties"), ("v_codes", "v_ties")):
         a = host(g[k])[dst]
+        if k == "k_codes":
+            a = k_codes_token_major(a)
         r = st2[k][dst]
         tie = st2[t][dst]
         bad = (a != r) & ~tie
@@ -121,6 +143,6 @@ def run_exact(B, Hkv, G, q, kpool_t, vpool_t, table, seq_len, sigma=1 / 16):
 
 
 def oracle_int8(O, Hkv, G, q, g, table, n_pages, sigma=1 / 16):
-    return O.decode_int8(q, host(g["k_codes"]), host(g["v_codes"]), host(g["k_chan"]), host(g["k_tok"]),
+    return O.decode_int8(q, k_codes_token_major(host(g["k_codes"])), host(g["v_codes"]), host(g["k_chan"]), host(g["k_tok"]),
                          host(g["v_chan"]), np.asarray(table, np.int32), np.asarray(n_pages, np.int32), Hkv, G,
                          sigma, mode=0)

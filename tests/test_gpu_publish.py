@@ -10,7 +10,7 @@ import torch
 
 from oracle import oracle as O
 from quantized_paged_kv_akv_amd import inputs
-from tests.gpu_util import check_attn, check_quantize, dev, host, say
+from tests.gpu_util import check_attn, check_quantize, dev, host, k_codes_token_major, say
 
 pytestmark = pytest.mark.gpu
 SIG = 1.0 / 16.0
@@ -125,7 +125,7 @@ def test_streaming_publication(B):
             qn = host(q[l].view(torch.int16)).view(np.uint16)
             n8s, wlen = st["n8"], st["wlen"]
             t8h = np.arange(max(1, n8s), dtype=np.int32).reshape(1, -1)
-            ro8, rl8 = O.decode_int8(qn, host(g["k_codes"]), host(g["v_codes"]), host(g["k_chan"]),
+            ro8, rl8 = O.decode_int8(qn, k_codes_token_major(host(g["k_codes"])), host(g["v_codes"]), host(g["k_chan"]),
                                      host(g["k_tok"]), host(g["v_chan"]), t8h, np.array([n8s], np.int32), Hkv, G,
                                      SIG, mode=0)
             twh = np.arange(n8s, cap, dtype=np.int32).reshape(1, -1)
