@@ -40,9 +40,10 @@ __device__ __forceinline__ u32x4 ld16(const T* p) {
 }
 
 // 16-byte load with the non-temporal (streaming) hint, for data read once
-// in whole 64-byte runs: on this part it moves the int8 pages about 6%
-// faster than the default policy.  Not for partial-line reads, whose other
-// half the default policy keeps cached for the next instruction.
+// in whole 64-byte runs (code tiles, per-page scales): on this part it moves
+// the int8 pages 6-9% faster than the default policy.  Not for partial-line
+// reads, whose other half the default policy keeps cached for the next
+// instruction (there the hint costs as much as it gains elsewhere).
 template <typename T>
 __device__ __forceinline__ u32x4 ld16_stream(const T* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));

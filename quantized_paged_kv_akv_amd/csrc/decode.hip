@@ -239,9 +239,9 @@ __device__ __forceinline__ void int8_split(const Int8Args& a, Int8Smem& sm, int 
         for (int s2 = 0; s2 < 4; ++s2)
 #pragma unroll
             for (int t = 0; t < 4; ++t) buf[4 * s2 + t] = ld16_stream(kp + koff + 1024 * (4 * s2 + t));
-        sk0 = ld16(a.kchan + sb * kD + 4 * l);
-        sv0 = ld16(a.vchan + sb * kD + 4 * l);
-        st0 = a.ktok[sb * kP + l];
+        sk0 = ld16_stream(a.kchan + sb * kD + 4 * l);
+        sv0 = ld16_stream(a.vchan + sb * kD + 4 * l);
+        st0 = __builtin_nontemporal_load(a.ktok + sb * kP + l);
     }
 
     // this wave's page slots, read once (the loop reads them from LDS)
@@ -294,9 +294,9 @@ __device__ __forceinline__ void int8_split(const Int8Args& a, Int8Smem& sm, int 
                 ns = page_base(p + 1);
                 nb = ns * (kP * kD);
                 knp = a.kc + nb;
-                skn = ld16(a.kchan + ns * kD + 4 * l);
-                svn = ld16(a.vchan + ns * kD + 4 * l);
-                stn = a.ktok[ns * kP + l];
+                skn = ld16_stream(a.kchan + ns * kD + 4 * l);
+                svn = ld16_stream(a.vchan + ns * kD + 4 * l);
+                stn = __builtin_nontemporal_load(a.ktok + ns * kP + l);
             }
             // S^T over all 256 channels: q' = q (.) c, hi + lo
             f32x4 S[4];
