@@ -186,12 +186,70 @@ __global__ __launch_bounds__(256) void combine_reg_kernel(int D, int n_splits, c
     }
 }
 
+// The same pass with 16-byte loads: block (row, 64 channels), 16 split lanes
+// x 16 threads x 4 channels, up to 16*K splits held in registers.
+template <int K>
+__global__ __launch_bounds__(256) void combine_vec_kernel(int D, int n_splits, const float* __restrict__ part_o,
+                                                          const float* __restrict__ part_lse,
+                                                          float* __restrict__ out_o, float* __restrict__ out_lse) {
+    const int r = blockIdx.x, chunk = blockIdx.y;
+    const int tid = threadIdx.x, sl = tid >> 4, c4 = 4 * (tid & 15);
+    const int d = chunk * 64 + c4;
+    __shared__ float red_m[16], red_w[16];
+    __shared__ f32x4 acc_s[16][16];
+    const float* lse = part_lse + (size_t)r * n_splits;
+    const float* po = part_o + (size_t)r * n_splits * D + d;
+    float l[K];
+    f32x4 o[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const int sp = sl + 16 * k;
+        l[k] = sp < n_splits ? lse[sp] : -INFINITY;
+        o[k] = sp < n_splits ? *reinterpret_cast<const f32x4*>(po + (size_t)sp * D) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    float m = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < K; ++k) m = fmaxf(m, l[k]);
+    if ((tid & 15) == 0) red_m[sl] = m;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 16; ++k) m = fmaxf(m, red_m[k]);
+    if (m == -INFINITY) {  // every split empty
+        if (sl == 0) *reinterpret_cast<f32x4*>(out_o + (size_t)r * D + d) = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        if (chunk == 0 && tid == 0) out_lse[r] = -INFINITY;
+        return;
+    }
+    float w = 0.0f;
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const float e = (l[k] == -INFINITY) ? 0.0f : expf(l[k] - m);
+        w += e;
+        if (e != 0.0f) acc += e * o[k];  // an empty split's O slot may hold anything
+    }
+    acc_s[sl][tid & 15] = acc;
+    if ((tid & 15) == 0) red_w[sl] = w;
+    __syncthreads();
+    if (sl == 0) {
+        f32x4 t = {0.0f, 0.0f, 0.0f, 0.0f};
+        float W = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            t += acc_s[k][tid];
+            W += red_w[k];
+        }
+        *reinterpret_cast<f32x4*>(out_o + (size_t)r * D + d) = t / W;
+        if (chunk == 0 && tid == 0) out_lse[r] = m + logf(W);
+    }
+}
+
 akv_status launch_combine(int rows, int D, const float* part_o, const float* part_lse, int n_splits, float* out_o,
                           float* out_lse, hipStream_t stream) {
     if (rows == 0) return AKV_OK;
     dim3 grid((unsigned)rows, (unsigned)(D / 32));
-    if (n_splits <= 8 * 16)
-        combine_reg_kernel<16><<<grid, 256, 0, stream>>>(D, n_splits, part_o, part_lse, out_o, out_lse);
+    if (n_splits <= 16 * 8)
+        combine_vec_kernel<8><<<dim3((unsigned)rows, (unsigned)(D / 64)), 256, 0, stream>>>(
+            D, n_splits, part_o, part_lse, out_o, out_lse);
     else if (n_splits <= 8 * 32)
         combine_reg_kernel<32><<<grid, 256, 0, stream>>>(D, n_splits, part_o, part_lse, out_o, out_lse);
     else
