@@ -354,3 +354,52 @@ def test_batched_full_size(B):
     d = inputs.make_layer_np(w, 1)
     say("case batched 32 requests, layer 1")
     _hybrid_layer(B, w, d, "batched32")
+
+
+def test_hybrid_step_replays_from_a_graph(B):
+    """A two-layer hybrid step captured in a HIP graph replays to the eager
+    result, several times, with eager work and synchronisations between the
+    replays (decode loops capture their step)."""
+    w = configs.ctx32k()
+    say("case hybrid step in a graph")
+    d8 = B.dims(4, 6)
+    layers = []
+    for li in (0, 1):
+        d = inputs.make_layer_np(w, li)
+        plan = d["plan"]
+        src, dst = plan.quant_src_dst()
+        g = gpu_quantize(B, d["k_pool"], d["v_pool"], src, dst, plan.int8_slots_total, 4)
+        layers.append((dev(d["q"]), g, dev(d["k_pool"]), dev(d["v_pool"])))
+    t8, tw = plan.int8_table(), plan.window_table()
+    tabs = (dev(t8), dev(np.asarray(plan.n8, np.int32)), dev(tw), dev(np.asarray(plan.win_tokens, np.int32)))
+    ws = torch.empty(B.akv_decode_hybrid_workspace_bytes(d8, 1, t8.shape[1], tw.shape[1]), dtype=torch.uint8,
+                     device="cuda")
+    outs = [(torch.zeros((1, 24, 256), device="cuda"), torch.zeros((1, 24), device="cuda")) for _ in layers]
+
+    def step():
+        for (q, g, kp, vp), (o, l) in zip(layers, outs):
+            B.akv_decode_hybrid(d8, 1, q, g["k_codes"], g["v_codes"], g["k_chan"], g["k_tok"], g["v_chan"],
+                                tabs[0], tabs[1], t8.shape[1], kp, vp, tabs[2], tabs[3], tw.shape[1], SIG, o, l, ws)
+    step()
+    torch.cuda.synchronize()
+    ref = [(o.clone(), l.clone()) for o, l in outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(4):
+        for o, l in outs:
+            o.fill_(float("nan"))
+            l.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for (o, l), (ro, rl) in zip(outs, ref):
+            assert torch.equal(o, ro) and torch.equal(l, rl), f"replay {rep} differs"
+        step()  # eager work between replays
+        torch.cuda.synchronize()
