@@ -12,6 +12,8 @@
  *   "SYCL" page, "A merge that joins the tiers"
  *       -- log-sum-exp output starting at -inf; merge into one FP32
  *          accumulator.
+ *   "Model quantization" page, "A lossless tier first"
+ *       -- the 13-bit lossless tier the 8-bit format replaced.
  *   "ActiveKV" page, "The idea" and "What I built"
  *       -- exact BF16 tier, hybrid tier, host-authoritative pinned history,
  *          budgeted staging with a fence-safe lifecycle, explicit refusal.
@@ -275,6 +277,71 @@ akv_status akv_tables_advance(int32_t batch, const int32_t *count, const int32_t
                               int32_t *int8_table, int32_t *n_pages_int8, int32_t max_pages_int8,
                               int32_t *window_table, int32_t *window_len, int32_t max_pages_window,
                               int32_t *status, void *stream);
+
+/*
+ * Lossless 13-bit tier ("Model quantization" page, "A lossless tier first":
+ * 13 bits per value, a 32-entry table per plane, a raw fallback for a plane
+ * that needs more).  A plane is one page of one KV head, keys or values
+ * (16,384 BF16 values).  Its table lists the plane's distinct BF16 high
+ * bytes (sign and the upper seven exponent bits) in ascending order, unused
+ * entries 0; each value is stored as the 5-bit position of its high byte in
+ * the table plus its low byte, 13 bits, so a coded plane takes 26,624 bytes.
+ * A plane with more than 32 distinct high bytes is stored raw: its 32,768
+ * bytes exactly as in the BF16 pool.  Decoding is exact for every bit
+ * pattern (NaN payloads, signed zeros, subnormals).
+ *
+ * Record storage (caller-owned device memory; record slots play the role
+ * of pool slots in page tables):
+ *   l13_desc   int32 [slot][Hkv][2]       (keys 0, values 1):
+ *              (byte offset of the plane in the arena / 256) << 1 | raw
+ *   l13_table  uint8 [slot][Hkv][2][32]
+ *   l13_arena  bytes, 256-byte aligned; planes at 256-byte aligned offsets.
+ * Inside a coded plane, lane slot (w, l, v) (w < 4, l < 64, v < 64; n = l % 16,
+ * g = l / 16) stands for
+ *   keys:    token 16 (n / 4) + 4 (v / 16) + n % 4, channel 64 w + 16 g + 8 ((v / 8) % 2) + v % 8
+ *   values:  channel 64 w + 16 ((v / 16) % 4) + n, token 16 g + 8 ((v / 8) % 2) + v % 8
+ * and its low byte is at byte ((4 w + v / 16) * 64 + l) * 16 + v % 16; bits
+ * 0-3 of its table position at byte 16384 + ((2 w + v / 32) * 64 + l) * 16
+ * + 4 ((v / 8) % 4) + v % 4 (low nibble when (v / 4) % 2 = 0, else high);
+ * bit 4 at byte 24576 + (w * 64 + l) * 8 + 4 (v / 32) + v % 4, bit (v / 4) % 8.
+ * (This is the order in which the decode kernel's lanes consume values.)
+ *
+ * akv_l13_encode_pages: encodes both planes of every KV head of BF16 pool
+ *   pages src_slot[i] into record slots dst_slot[i] (i < n; dst slots
+ *   distinct).  Planes are packed back to back from byte arena_offset
+ *   (a multiple of 256) in the order (i, head, keys then values); coded
+ *   planes take 26,624 bytes, raw ones 32,768.  The call is refused with
+ *   AKV_ERR_BUDGET, nothing enqueued, unless arena_offset + n * Hkv * 2 *
+ *   32,768 <= arena_bytes (room even if every plane is raw); offsets must
+ *   stay below 256 GiB.  *arena_end (device int64, 8-byte aligned) receives
+ *   the byte offset just past the last plane (arena_offset when n = 0): the
+ *   arena_offset of a following call, and the byte count to stage.  Three
+ *   kernels on `stream`; src_slot and dst_slot are device int32 arrays.
+ *   Errors: AKV_ERR_ARG, AKV_ERR_UNSUPPORTED, AKV_ERR_ALIGN, AKV_ERR_BUDGET.
+ * akv_l13_decode_pages: writes record slots src_slot[i] back into BF16 pool
+ *   slots dst_slot[i] (both planes, every head), bit-exactly.
+ *   Errors: AKV_ERR_ARG, AKV_ERR_UNSUPPORTED, AKV_ERR_ALIGN.
+ * akv_decode_attn_l13: akv_decode_attn_exact over 13-bit records, reading
+ *   them directly (coded planes are expanded to BF16 in registers, raw
+ *   planes read as BF16); page_table holds record slots.  Same split plan and
+ *   arithmetic as akv_decode_attn_exact, so the result is bit-identical to it
+ *   on the decoded pages.  Descriptors must come from akv_l13_encode_pages.
+ *   workspace: at least akv_decode_workspace_bytes(dims, batch, max_pages).
+ *   Errors as akv_decode_attn_exact (the arena must be 256-byte aligned).
+ */
+akv_status akv_l13_encode_pages(const akv_dims *dims, int32_t n, const uint16_t *k_bf16, const uint16_t *v_bf16,
+                                const int32_t *src_slot, const int32_t *dst_slot,
+                                uint8_t *l13_arena, int64_t arena_offset, int64_t arena_bytes,
+                                int32_t *l13_desc, uint8_t *l13_table, int64_t *arena_end, void *stream);
+akv_status akv_l13_decode_pages(const akv_dims *dims, int32_t n, const uint8_t *l13_arena,
+                                const int32_t *l13_desc, const uint8_t *l13_table,
+                                const int32_t *src_slot, const int32_t *dst_slot,
+                                uint16_t *k_bf16, uint16_t *v_bf16, void *stream);
+akv_status akv_decode_attn_l13(const akv_dims *dims, int32_t batch, const uint16_t *q,
+                               const uint8_t *l13_arena, const int32_t *l13_desc, const uint8_t *l13_table,
+                               const int32_t *page_table, const int32_t *seq_len, int32_t max_pages,
+                               float softmax_scale, float *out_o, float *out_lse,
+                               void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Host-staged mode ("ActiveKV" page, "The idea" and "What I built"): the

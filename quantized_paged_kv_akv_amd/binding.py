@@ -28,6 +28,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
 _sz = ctypes.c_size_t
+_i64 = ctypes.c_int64
 _f32 = ctypes.c_float
 
 
@@ -60,6 +61,10 @@ _SIGS = {
     "akv_stream_read": (ctypes.c_int, [_vp, _sz, _vp, _vp]),
     "akv_publish_pages": (ctypes.c_int, [_D, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "akv_tables_advance": (ctypes.c_int, [_i32, _vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp]),
+    "akv_l13_encode_pages": (ctypes.c_int, [_D, _i32, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp]),
+    "akv_l13_decode_pages": (ctypes.c_int, [_D, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "akv_decode_attn_l13": (ctypes.c_int, [_D, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _f32, _vp, _vp, _vp,
+                                           _sz, _vp]),
     "akv_ring_create": (ctypes.c_int, [ctypes.POINTER(_vp), _sz, _i32, ctypes.POINTER(_vp)]),
     "akv_ring_stage": (ctypes.c_int, [_vp, _i32, ctypes.POINTER(_vp), ctypes.POINTER(_sz), _i32, _vp, _vp,
                                       ctypes.POINTER(_vp), ctypes.POINTER(_sz)]),
@@ -194,6 +199,43 @@ def akv_merge_lse(rows: int, head_dim: int, acc_o, acc_lse, part_o, part_lse, st
 def akv_fill_empty(rows: int, head_dim: int, o, lse, stream=None):
     _check("akv_fill_empty", _lib.akv_fill_empty(rows, head_dim, _ptr(o, torch.float32, "o"),
                                                  _ptr(lse, torch.float32, "lse"), _stream(stream)))
+
+
+def l13_sizes(d: akv_dims, slots: int) -> dict:
+    """Shapes of the 13-bit record arrays for `slots` record slots, and the
+    arena bytes that always suffice (every plane raw)."""
+    return dict(desc=(slots, d.num_kv_heads, 2), table=(slots, d.num_kv_heads, 2, 32),
+                arena_bytes=slots * d.num_kv_heads * 2 * 32768)
+
+
+def akv_l13_encode_pages(d: akv_dims, n: int, k_bf16, v_bf16, src_slot, dst_slot, arena, arena_offset: int,
+                         desc, table, arena_end, stream=None):
+    """arena: a device uint8 tensor (its size is the capacity)."""
+    _check("akv_l13_encode_pages", _lib.akv_l13_encode_pages(
+        ctypes.byref(d), n, _ptr(k_bf16, _BF16, "k_bf16"), _ptr(v_bf16, _BF16, "v_bf16"),
+        _ptr(src_slot, torch.int32, "src_slot"), _ptr(dst_slot, torch.int32, "dst_slot"),
+        _ptr(arena, torch.uint8, "arena"), arena_offset, arena.numel(), _ptr(desc, torch.int32, "desc"),
+        _ptr(table, torch.uint8, "table"), _ptr(arena_end, torch.int64, "arena_end"), _stream(stream)))
+
+
+def akv_l13_decode_pages(d: akv_dims, n: int, arena, desc, table, src_slot, dst_slot, k_bf16, v_bf16,
+                         stream=None):
+    _check("akv_l13_decode_pages", _lib.akv_l13_decode_pages(
+        ctypes.byref(d), n, _ptr(arena, torch.uint8, "arena"), _ptr(desc, torch.int32, "desc"),
+        _ptr(table, torch.uint8, "table"), _ptr(src_slot, torch.int32, "src_slot"),
+        _ptr(dst_slot, torch.int32, "dst_slot"), _ptr(k_bf16, _BF16, "k_bf16"), _ptr(v_bf16, _BF16, "v_bf16"),
+        _stream(stream)))
+
+
+def akv_decode_attn_l13(d: akv_dims, batch: int, q, arena, desc, table, page_table, seq_len, max_pages: int,
+                        softmax_scale: float, out_o, out_lse, workspace, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("akv_decode_attn_l13", _lib.akv_decode_attn_l13(
+        ctypes.byref(d), batch, _ptr(q, _BF16, "q"), _ptr(arena, torch.uint8, "arena"),
+        _ptr(desc, torch.int32, "desc"), _ptr(table, torch.uint8, "table"),
+        _ptr(page_table, torch.int32, "page_table"), _ptr(seq_len, torch.int32, "seq_len"), max_pages,
+        softmax_scale, _ptr(out_o, torch.float32, "out_o"), _ptr(out_lse, torch.float32, "out_lse"),
+        _ptr(workspace, (torch.uint8, torch.int8, torch.float32), "workspace"), ws_bytes, _stream(stream)))
 
 
 def _event(e) -> _vp:

@@ -16,7 +16,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libakv.so")
-SOURCES = ["akv_host.cpp", "merge.hip", "quantize.hip", "decode.hip", "ring.cpp", "calib.hip", "publish.hip"]
+SOURCES = ["akv_host.cpp", "merge.hip", "quantize.hip", "decode.hip", "ring.cpp", "calib.hip", "publish.hip", "lossless.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

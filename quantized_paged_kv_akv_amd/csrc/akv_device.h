@@ -133,6 +133,128 @@ __device__ __forceinline__ void split_bf16(float x, __bf16& hi, __bf16& lo) {
     lo = (__bf16)(x - (float)hi);
 }
 
+// Exact-tier page order: QK tile t, A-operand row i is token
+// 16 (i / 4) + 4 t + i % 4 of the page.
+__host__ __device__ __forceinline__ int qk_row_token(int t, int i) { return 16 * (i >> 2) + 4 * t + (i & 3); }
+
+// BF16 page-head loads of lane (w, n, g): key register 2t + s is token
+// qk_row_token(t, n) at channels 64w + 16g + 8s .. + 8; value register 2j + s
+// is channel 64w + 16j + n at tokens 16g + 8s .. + 8.
+__device__ __forceinline__ void bf16_keys_load(const uint16_t* kp, int w, int n, int g, u32x4 (&K)[8]) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) K[2 * t + s] = ld16(kp + qk_row_token(t, n) * kD + 64 * w + 16 * g + 8 * s);
+}
+__device__ __forceinline__ void bf16_values_load(const uint16_t* vp, int w, int n, int g, u32x4 (&V)[8]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) V[2 * j + s] = ld16(vp + (64 * w + 16 * j + n) * kP + 16 * g + 8 * s);
+}
+
+// BF16 stores mirroring the loads above.
+__device__ __forceinline__ void bf16_keys_store(uint16_t* kp, int w, int n, int g, const u32x4 (&K)[8]) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+            *reinterpret_cast<u32x4*>(kp + qk_row_token(t, n) * kD + 64 * w + 16 * g + 8 * s) = K[2 * t + s];
+}
+__device__ __forceinline__ void bf16_values_store(uint16_t* vp, int w, int n, int g, const u32x4 (&V)[8]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+            *reinterpret_cast<u32x4*>(vp + (64 * w + 16 * j + n) * kP + 16 * g + 8 * s) = V[2 * j + s];
+}
+
+// ---------------------------------------------------------------- 13-bit planes
+// Lossless 13-bit plane ("Model quantization" page, "A lossless tier first"):
+// each BF16 value is the 5-bit position of its high byte (sign and upper
+// seven exponent bits) in the plane's 32-entry table, plus its low byte.
+// Storage follows the lane that consumes the value: lane slot (w, l, v) --
+// wave w, lane l, value v < 64 of that lane -- is, for a key plane, token
+// 16 (n / 4) + 4 (v / 16) + n % 4 at channel 64 w + 16 g + 8 ((v / 8) % 2)
+// + v % 8, and for a value plane channel 64 w + 16 ((v / 16) % 4) + n at
+// token 16 g + 8 ((v / 8) % 2) + v % 8 (n = l % 16, g = l / 16): the 8
+// values of operand register r = v / 8 are exactly what the BF16 pool's
+// 16-byte load r gives that lane in the exact tier's body.
+// A coded plane is 26,624 bytes: 16 KB of low bytes, 8 KB of index nibbles,
+// 2 KB of index bit 4.
+constexpr int kL13PlaneBytes = 26624;
+constexpr int kL13RawBytes = kP * kD * 2;
+constexpr int kL13NibbleBase = 16384;
+constexpr int kL13HighBase = 24576;
+
+// Byte offsets of lane (w, l)'s chunks: low bytes chunk q < 4 (values
+// 16q .. 16q + 15), nibble chunk h < 2 (values 32h .. 32h + 31; u32 word k
+// holds values 32h + 8k + b in the low nibble of byte b and 32h + 8k + 4 + b
+// in the high nibble), index bit 4 (u32 word k < 2 covers values 32k ..
+// 32k + 31: value 32k + i sits at bit 8 (i % 4) + i / 4).
+__host__ __device__ __forceinline__ int l13_low_offset(int w, int l, int q) { return ((4 * w + q) * 64 + l) * 16; }
+__host__ __device__ __forceinline__ int l13_nibble_offset(int w, int l, int h) {
+    return kL13NibbleBase + ((2 * w + h) * 64 + l) * 16;
+}
+__host__ __device__ __forceinline__ int l13_high_offset(int w, int l) { return kL13HighBase + (w * 64 + l) * 8; }
+
+// Byte offset of the 16 bytes lane (w, l) loads into register r of a coded
+// plane: low-byte chunks (r < 4), nibble chunks (r = 4, 5), and for r >= 6
+// the aligned 16 bytes holding the index-bit-4 words of lanes l & ~1 and
+// l | 1 (the lane's own 8 bytes are the first half for even l, the second
+// for odd l).  Every load stays inside the plane's 26,624 bytes.
+__host__ __device__ __forceinline__ int l13_chunk_offset(int w, int l, int r) {
+    return r < 4 ? l13_low_offset(w, l, r) : r < 6 ? l13_nibble_offset(w, l, r - 4) : l13_high_offset(w, l & ~1);
+}
+
+// A lane's coded values: c[0..3] low-byte chunks, c[4..5] nibble chunks,
+// c[6] index bit 4 of values 0..31 / 32..63 in .x / .y (even lanes) or
+// .z / .w (odd lanes); c[7] is not used.
+__device__ __forceinline__ void l13_load(const uint8_t* plane, int w, int l, u32x4 (&c)[8]) {
+#pragma unroll
+    for (int r = 0; r < 7; ++r) c[r] = ld16_stream(plane + l13_chunk_offset(w, l, r));
+    c[7] = c[6];
+}
+
+// Table entry per byte: byte b of the result is T[idx_b] (idx_b < 32), with
+// the table as 8 little-endian words.  Three levels of byte permutes: the
+// low three index bits pick within 8-entry groups, bits 3 and 4 pick groups.
+__device__ __forceinline__ uint32_t l13_lookup(const uint32_t (&T)[8], uint32_t idx) {
+    const uint32_t sel = idx & 0x07070707u;
+    const uint32_t p0 = __builtin_amdgcn_perm(T[1], T[0], sel);
+    const uint32_t p1 = __builtin_amdgcn_perm(T[3], T[2], sel);
+    const uint32_t p2 = __builtin_amdgcn_perm(T[5], T[4], sel);
+    const uint32_t p3 = __builtin_amdgcn_perm(T[7], T[6], sel);
+    const uint32_t s3 = ((idx >> 1) & 0x04040404u) | 0x03020100u;
+    const uint32_t q0 = __builtin_amdgcn_perm(p1, p0, s3);
+    const uint32_t q1 = __builtin_amdgcn_perm(p3, p2, s3);
+    const uint32_t s4 = ((idx >> 2) & 0x04040404u) | 0x03020100u;
+    return __builtin_amdgcn_perm(q1, q0, s4);
+}
+
+// Bit j (0..7) of each byte of H moved to bit 4.
+__device__ __forceinline__ uint32_t l13_bit4(uint32_t H, int j) {
+    return (j <= 4 ? H << (4 - j) : H >> (j - 4)) & 0x10101010u;
+}
+
+// BF16 operand register r (values 8r .. 8r + 7 of the lane) of a coded
+// plane; odd = lane index is odd.
+__device__ __forceinline__ u32x4 l13_operand(const u32x4 (&c)[8], const uint32_t (&T)[8], int r, bool odd) {
+    const u32x4 lo = c[r >> 1];
+    const uint32_t L0 = (r & 1) ? lo.z : lo.x;
+    const uint32_t L1 = (r & 1) ? lo.w : lo.y;
+    const u32x4 nb = c[4 + (r >> 2)];
+    const int k = r & 3;
+    const uint32_t N = k == 0 ? nb.x : k == 1 ? nb.y : k == 2 ? nb.z : nb.w;
+    const uint32_t H = (r >> 2) ? (odd ? c[6].w : c[6].y) : (odd ? c[6].z : c[6].x);
+    const uint32_t i0 = (N & 0x0F0F0F0Fu) | l13_bit4(H, 2 * k);
+    const uint32_t i1 = ((N >> 4) & 0x0F0F0F0Fu) | l13_bit4(H, 2 * k + 1);
+    const uint32_t E0 = l13_lookup(T, i0), E1 = l13_lookup(T, i1);
+    // value pairs: low byte from L, high byte from E
+    return u32x4{__builtin_amdgcn_perm(E0, L0, 0x05010400u), __builtin_amdgcn_perm(E0, L0, 0x07030602u),
+                 __builtin_amdgcn_perm(E1, L1, 0x05010400u), __builtin_amdgcn_perm(E1, L1, 0x07030602u)};
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 

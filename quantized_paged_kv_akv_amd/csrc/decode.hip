@@ -78,9 +78,6 @@ struct ExactSmem {
     float part[2][4][16][64];  // QK partial logits of the four waves, double-buffered
 };
 
-// QK tile t, A-operand row i  ->  token within the page
-__device__ __forceinline__ int qk_row_token(int t, int i) { return 16 * (i >> 2) + 4 * t + (i & 3); }
-
 // Sum the four waves' partial logits for this lane: tile t, row r is token
 // 16g + 4t + r of the page.
 __device__ __forceinline__ void gather_logits(const float (*part)[16][64], int l, float S[16]) {
@@ -451,7 +448,99 @@ __device__ __forceinline__ u32x4 mask_tokens(u32x4 v, int first, int limit) {
     return u32x4{wd[0], wd[1], wd[2], wd[3]};
 }
 
-__device__ __forceinline__ void exact_split(const ExactArgs& a, ExactSmem& sm, int split, int kvh, int b) {
+// Operand sources of the exact body.  load() fetches one page-head's
+// registers for this lane (the next page's while the current one is in
+// use); keys() and values() hand the eight BF16 operand registers, in
+// order, to f.
+struct Bf16Source {  // the BF16 pool: the loaded registers are the operands
+    const uint16_t* kb;
+    const uint16_t* vb;
+    struct Page {
+        u32x4 k[8], v[8];
+    };
+    __device__ __forceinline__ void load(int slot, int kvh, int Hkv, int w, int l, Page& R) const {
+        const size_t base = ((size_t)slot * Hkv + kvh) * (kP * kD);
+        bf16_keys_load(kb + base, w, l & 15, l >> 4, R.k);
+        bf16_values_load(vb + base, w, l & 15, l >> 4, R.v);
+    }
+    template <class F>
+    __device__ __forceinline__ void keys(const Page& R, F&& f) const {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) f(r, R.k[r]);
+    }
+    template <class F>
+    __device__ __forceinline__ void values(const Page& R, F&& f) const {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) f(r, R.v[r]);
+    }
+};
+
+// The lossless 13-bit planes ("Model quantization" page, "A lossless tier
+// first"): per plane a descriptor ((byte offset / 256) << 1 | raw) and a
+// 32-entry table; a coded plane is expanded to BF16 in registers right
+// before its MFMA, a raw plane is read as the BF16 pool is.
+struct L13Source {
+    const uint8_t* arena;
+    const int32_t* desc;
+    const uint8_t* table;
+    struct Page {
+        u32x4 k[8], v[8];
+        uint32_t tk[8], tv[8];
+        int raw_k, raw_v;
+        bool odd;  // lane parity (selects the lane's half of the index-bit-4 load)
+    };
+    __device__ __forceinline__ void load(int slot, int kvh, int Hkv, int w, int l, Page& R) const {
+        const size_t plane = ((size_t)slot * Hkv + kvh) * 2;
+        const int dk = __builtin_amdgcn_readfirstlane(desc[plane]);
+        const int dv = __builtin_amdgcn_readfirstlane(desc[plane + 1]);
+        const uint32_t* tp = reinterpret_cast<const uint32_t*>(table + plane * 32);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            R.tk[i] = __builtin_amdgcn_readfirstlane(tp[i]);
+            R.tv[i] = __builtin_amdgcn_readfirstlane(tp[8 + i]);
+        }
+        R.raw_k = dk & 1;
+        R.raw_v = dv & 1;
+        R.odd = l & 1;
+        const uint8_t* kp = arena + (size_t)(dk >> 1) * 256;
+        const uint8_t* vp = arena + (size_t)(dv >> 1) * 256;
+        const int n = l & 15, g = l >> 4;
+        // one 16-byte load per register either way (the choice of address is
+        // uniform): a raw plane's BF16 operand, or a coded plane's chunk
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const int coded = l13_chunk_offset(w, l, r);
+            const int rk = 2 * (qk_row_token(r >> 1, n) * kD + 64 * w + 16 * g + 8 * (r & 1));
+            const int rv = 2 * ((64 * w + 16 * (r >> 1) + n) * kP + 16 * g + 8 * (r & 1));
+            R.k[r] = ld16_stream(kp + (R.raw_k ? rk : coded));
+            R.v[r] = ld16_stream(vp + (R.raw_v ? rv : coded));
+        }
+    }
+    template <class F>
+    __device__ __forceinline__ void keys(const Page& R, F&& f) const {
+        if (R.raw_k) {
+#pragma unroll
+            for (int r = 0; r < 8; ++r) f(r, R.k[r]);
+        } else {
+#pragma unroll
+            for (int r = 0; r < 8; ++r) f(r, l13_operand(R.k, R.tk, r, R.odd));
+        }
+    }
+    template <class F>
+    __device__ __forceinline__ void values(const Page& R, F&& f) const {
+        if (R.raw_v) {
+#pragma unroll
+            for (int r = 0; r < 8; ++r) f(r, R.v[r]);
+        } else {
+#pragma unroll
+            for (int r = 0; r < 8; ++r) f(r, l13_operand(R.v, R.tv, r, R.odd));
+        }
+    }
+};
+
+template <class Src>
+__device__ __forceinline__ void exact_split(const ExactArgs& a, const Src& src, ExactSmem& sm, int split, int kvh,
+                                            int b) {
     const int len = a.seq_len[b];
     const int np = min((len + kP - 1) / kP, a.max_pages);
     const int p0 = split * a.pps;
@@ -483,22 +572,8 @@ __device__ __forceinline__ void exact_split(const ExactArgs& a, ExactSmem& sm, i
         qb[1] = as_bf16x8(q1);
     }
 
-    u32x4 kr[8], vr[8];
-    auto load_codes = [&](int p, u32x4 (&K)[8], u32x4 (&V)[8]) {
-        const size_t base = ((size_t)pt[p] * Hkv + kvh) * (kP * kD);
-        const uint16_t* kb = a.kb + base;
-        const uint16_t* vb = a.vb + base;
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int s = 0; s < 2; ++s) K[2 * t + s] = ld16(kb + qk_row_token(t, n) * kD + 64 * w + 16 * g + 8 * s);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int s = 0; s < 2; ++s) V[2 * j + s] = ld16(vb + (64 * w + 16 * j + n) * kP + 16 * g + 8 * s);
-    };
-
-    load_codes(p0, kr, vr);
+    typename Src::Page cur;
+    src.load(pt[p0], kvh, Hkv, w, l, cur);
 
     float M = -INFINITY, lsum = 0.0f;
     f32x4 O[4];
@@ -508,17 +583,18 @@ __device__ __forceinline__ void exact_split(const ExactArgs& a, ExactSmem& sm, i
     int it = 0;
     for (int p = p0; p < p1; ++p, ++it) {
         const bool has_next = p + 1 < p1;
-        u32x4 kn[8], vn[8];
-        if (has_next) load_codes(p + 1, kn, vn);
+        typename Src::Page nxt;
+        if (has_next) src.load(pt[p + 1], kvh, Hkv, w, l, nxt);
 
+        f32x4 acc[4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-            acc = mfma_bf16(as_bf16x8(kr[2 * t]), qb[0], acc);
-            acc = mfma_bf16(as_bf16x8(kr[2 * t + 1]), qb[1], acc);
+        for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        // key register 2t + s is tile t, contraction half s
+        src.keys(cur, [&](int r, u32x4 kop) { acc[r >> 1] = mfma_bf16(as_bf16x8(kop), qb[r & 1], acc[r >> 1]); });
 #pragma unroll
-            for (int r = 0; r < 4; ++r) s_part[it & 1][w][4 * t + r][l] = acc[r];
-        }
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s_part[it & 1][w][4 * t + r][l] = acc[t][r];
         __syncthreads();
 
         const int in_page = len - p * kP;  // valid tokens in this page (>= 1)
@@ -538,26 +614,17 @@ __device__ __forceinline__ void exact_split(const ExactArgs& a, ExactSmem& sm, i
                 pb[s][e2] = valid ? (hi_lane ? hi : lo) : (__bf16)0.0f;
             }
 
-        if (in_page < kP) {  // last, partial page: masked values must not reach the MFMA
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int s = 0; s < 2; ++s) vr[2 * j + s] = mask_tokens(vr[2 * j + s], 16 * g + 8 * s, in_page);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            O[j] = O[j] * alpha;
-            O[j] = mfma_bf16(as_bf16x8(vr[2 * j]), pb[0], O[j]);
-            O[j] = mfma_bf16(as_bf16x8(vr[2 * j + 1]), pb[1], O[j]);
-        }
+        for (int j = 0; j < 4; ++j) O[j] = O[j] * alpha;
+        // value register 2j + s is channel tile j, contraction half s (tokens 16g + 8s ..);
+        // on the last, partial page masked values must not reach the MFMA
+        const bool partial = in_page < kP;
+        src.values(cur, [&](int r, u32x4 vop) {
+            if (partial) vop = mask_tokens(vop, 16 * g + 8 * (r & 1), in_page);
+            O[r >> 1] = mfma_bf16(as_bf16x8(vop), pb[r & 1], O[r >> 1]);
+        });
 
-        if (has_next) {
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                kr[k] = kn[k];
-                vr[k] = vn[k];
-            }
-        }
+        if (has_next) cur = nxt;
     }
 
     write_partial(O, M, lsum, valid, hi_lane, w, g, row, a.n_cols, a.col0 + split, a.part_o, a.part_lse);
@@ -575,7 +642,15 @@ __global__ __launch_bounds__(kThreads, 2) void decode_int8_kernel(Int8Args a) {
 
 __global__ __launch_bounds__(kThreads, 2) void decode_exact_kernel(ExactArgs a) {
     __shared__ ExactSmem sm;
-    exact_split(a, sm, blockIdx.x, blockIdx.y, blockIdx.z);
+    exact_split(a, Bf16Source{a.kb, a.vb}, sm, blockIdx.x, blockIdx.y, blockIdx.z);
+}
+
+// The exact body over lossless 13-bit planes: same split plan and
+// arithmetic as decode_exact_kernel, so the result is bit-identical to it on
+// the decoded pages.
+__global__ __launch_bounds__(kThreads, 2) void decode_l13_kernel(ExactArgs a, L13Source src) {
+    __shared__ ExactSmem sm;
+    exact_split(a, src, sm, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 // Both tiers of a layer in one launch: the first nw work-groups of each row
@@ -585,7 +660,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_exact_kernel(ExactArgs a) 
 __global__ __launch_bounds__(kThreads, 2) void decode_hybrid_kernel(Int8Args a8, ExactArgs ax, int nw) {
     __shared__ SplitSmem sm;
     if ((int)blockIdx.x < nw)
-        exact_split(ax, sm.ex, blockIdx.x, blockIdx.y, blockIdx.z);
+        exact_split(ax, Bf16Source{ax.kb, ax.vb}, sm.ex, blockIdx.x, blockIdx.y, blockIdx.z);
     else
         int8_split(a8, sm.i8, blockIdx.x - nw, blockIdx.y, blockIdx.z);
 }
@@ -786,4 +861,32 @@ extern "C" akv_status akv_decode_hybrid(const akv_dims* dims, int32_t batch, con
     launch_split(decode_hybrid_kernel, grid, s, a8, ax, pw.n_splits);
     if ((st = launch_status("decode_hybrid_kernel")) != AKV_OK) return st;
     return launch_combine(rows, dims->head_dim, a8.part_o, a8.part_lse, n_cols, out_o, out_lse, s);
+}
+
+extern "C" akv_status akv_decode_attn_l13(const akv_dims* dims, int32_t batch, const uint16_t* q,
+                                          const uint8_t* l13_arena, const int32_t* l13_desc,
+                                          const uint8_t* l13_table, const int32_t* page_table,
+                                          const int32_t* seq_len, int32_t max_pages, float softmax_scale,
+                                          float* out_o, float* out_lse, void* workspace, size_t workspace_bytes,
+                                          void* stream) {
+    clear_error();
+    akv_status st = check_shape(dims, batch, max_pages);
+    if (st != AKV_OK || batch == 0) return st;
+    if ((uintptr_t)l13_arena % 256 != 0) return fail(AKV_ERR_ALIGN, "l13_arena not 256-byte aligned");
+    const void* ptrs[] = {q, l13_arena, l13_table, out_o, out_lse};
+    const void* tabs[] = {page_table, seq_len, l13_desc};
+    if ((st = check_ptrs(ptrs, 5, tabs, 3)) != AKV_OK) return st;
+    const int rows = batch * dims->num_kv_heads * dims->group;
+    if (max_pages == 0) return akv_fill_empty(rows, dims->head_dim, out_o, out_lse, stream);
+    const SplitPlan plan = plan_splits(dims, batch, max_pages);
+    if ((st = check_workspace(workspace, workspace_bytes, partial_bytes(dims, batch, plan.n_splits))) != AKV_OK)
+        return st;
+    hipStream_t s = (hipStream_t)stream;
+    ExactArgs a = exact_args(dims, q, nullptr, nullptr, page_table, seq_len, max_pages, softmax_scale, plan);
+    split_workspace(dims, batch, plan.n_splits, workspace, &a.part_o, &a.part_lse);
+    const L13Source src{l13_arena, l13_desc, l13_table};
+    dim3 grid((unsigned)plan.n_splits, (unsigned)dims->num_kv_heads, (unsigned)batch);
+    launch_split(decode_l13_kernel, grid, s, a, src);
+    if ((st = launch_status("decode_l13_kernel")) != AKV_OK) return st;
+    return launch_combine(rows, dims->head_dim, a.part_o, a.part_lse, plan.n_splits, out_o, out_lse, s);
 }
