@@ -159,9 +159,10 @@ def run_gpu(args, w):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / steps
 
-    def split_kernel_us(fn, steps):
-        """Average duration of the split-K kernel of each decode call, from HIP
-        events the library records around that kernel on `stream`."""
+    def split_kernel_us(fn, steps, name):
+        """Average duration of the split-K kernel of each decode call (entry
+        point `name`), from HIP events the library records around that kernel
+        on `stream`."""
         evs = []
         for _ in range(steps):
             for i in range(w.layers):
@@ -171,7 +172,7 @@ def run_gpu(args, w):
                 evs.append((a, b))
         torch.cuda.synchronize()
         it = iter(evs)
-        orig = B.akv_decode_hybrid if fn is hybrid_step else B.akv_decode_attn_exact
+        orig = getattr(B, name)
 
         def hooked(*args, **kw):
             a, b = next(it)
@@ -180,7 +181,6 @@ def run_gpu(args, w):
                 orig(*args, **kw)
             finally:
                 B.akv_set_profile_events(None, None)
-        name = "akv_decode_hybrid" if fn is hybrid_step else "akv_decode_attn_exact"
         setattr(B, name, hooked)
         try:
             for _ in range(steps):
@@ -193,7 +193,7 @@ def run_gpu(args, w):
 
     log("[bench] hybrid step (fused entry) warmup + timed")
     ms_hybrid = timed(hybrid_step, args.steps, args.warmup)
-    hyb_us = split_kernel_us(hybrid_step, max(2, args.steps // 2))
+    hyb_us = split_kernel_us(hybrid_step, max(2, args.steps // 2), "akv_decode_hybrid")
     owners = {}
     if batch > 1:
         # the same step as launches of two requests (pairs with equal page
@@ -217,7 +217,49 @@ def run_gpu(args, w):
     ms_four = timed(four_call_step, max(2, args.steps // 2), 1)
     log("[bench] all-BF16 step")
     ms_bf16 = timed(bf16_step, max(2, args.steps // 2), 1)
-    bf16_us = split_kernel_us(bf16_step, 2)
+    bf16_us = split_kernel_us(bf16_step, 2, "akv_decode_attn_exact")
+
+    # lossless 13-bit tier, HBM-resident: each layer's whole history encoded
+    # (akv_l13_encode_pages), then decoded directly by akv_decode_attn_l13
+    log("[bench] lossless 13-bit tier: encode every layer, then the all-13-bit step")
+    l13_enc_ms, l13_read = [], 0
+    for L in layers:
+        n = L["k_pool"].shape[0]
+        sz = B.l13_sizes(dims, n)
+        rec = dict(arena=torch.empty(sz["arena_bytes"], dtype=torch.uint8, device=device),
+                   desc=torch.empty(sz["desc"], dtype=torch.int32, device=device),
+                   table=torch.empty(sz["table"], dtype=torch.uint8, device=device),
+                   end=torch.empty(1, dtype=torch.int64, device=device))
+        sl = torch.arange(n, dtype=torch.int32, device=device)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        B.akv_l13_encode_pages(dims, n, L["k_pool"], L["v_pool"], sl, sl, rec["arena"], 0, rec["desc"],
+                               rec["table"], rec["end"], stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        l13_enc_ms.append(e0.elapsed_time(e1))
+        L["l13"] = rec
+    l13_arena = [int(L["l13"]["end"][0]) for L in layers]
+    n_planes = layers[0]["k_pool"].shape[0] * Hkv * 2
+    # bytes one launch reads: the used planes, plus a descriptor and a table per plane
+    l13_layer_bytes = l13_arena[0] + n_planes * (4 + 32)
+    l13_raw = sum(int((L["l13"]["desc"] & 1).sum()) for L in layers)
+
+    def l13_step():
+        for i, L in enumerate(layers):
+            B.akv_decode_attn_l13(dims, batch, L["q"], L["l13"]["arena"], L["l13"]["desc"], L["l13"]["table"],
+                                  T["tf"], T["nf"], mf, sigma, out[i], outl[i], ws, stream)
+
+    ms_l13 = timed(l13_step, max(2, args.steps // 2), 1)
+    l13_us = split_kernel_us(l13_step, 2, "akv_decode_attn_l13")
+    l13_enc = sorted(l13_enc_ms)[len(l13_enc_ms) // 2]
+    lossless = dict(ms_step=ms_l13, launch_us=l13_us, bytes_per_launch=l13_layer_bytes,
+                    arena_bytes_per_layer=l13_arena[0], arena_frac_of_bf16=l13_arena[0] / by_layer_bf16(plan, Hkv),
+                    raw_planes=l13_raw, planes=n_planes * w.layers, encode_ms_per_layer=l13_enc,
+                    encode_GBps_in=by_layer_bf16(plan, Hkv) / (l13_enc * 1e-3) / 1e9)
+    for L in layers:
+        del L["l13"]
+    torch.cuda.empty_cache()
 
     # spread of single steps (events around each of a few more steps)
     step_us = []
@@ -258,7 +300,12 @@ def run_gpu(args, w):
                 bf16_bytes=bf16_bytes, hyb_launch_us=hyb_us, hyb_bytes_per_launch=layer_bytes,
                 hyb_achieved_gbps=layer_bytes / (hyb_us * 1e-6) / 1e9,
                 bf16_launch_us=bf16_us, bf16_achieved_gbps=by["bf16_all"] / (bf16_us * 1e-6) / 1e9,
-                quant_ms_per_layer=quant_ms, quant_gbps=quant_bytes / (quant_ms * 1e-3) / 1e9)
+                quant_ms_per_layer=quant_ms, quant_gbps=quant_bytes / (quant_ms * 1e-3) / 1e9, lossless=lossless)
+
+
+def by_layer_bf16(plan, Hkv) -> int:
+    """BF16 bytes of one layer's whole history (keys and values)."""
+    return step_kv_bytes(plan, Hkv)["bf16_all"]
 
 
 def run_staged(args, w):
@@ -266,7 +313,9 @@ def run_staged(args, w):
     is staged into a two-slot device ring on a side stream (events guard slot
     reuse), overlapped with the previous layer's attention.  The hybrid step
     stages the int8 pool (codes + scales) and the BF16 window pages; the
-    all-BF16 step stages the whole BF16 pool."""
+    all-BF16 step stages the whole BF16 pool; the lossless step stages the
+    whole history in the 13-bit format (packed planes, descriptors, tables)
+    and decodes it with akv_decode_attn_l13."""
     import torch
 
     from quantized_paged_kv_akv_amd import binding as B
@@ -302,15 +351,29 @@ def run_staged(args, w):
             blk[o:o + n].copy_(t.contiguous().view(-1).view(torch.uint8))
         return blk, [(o, t.dtype, tuple(t.shape)) for t, o in zip(ts, offs)]
 
-    log("[bench] copying the history to pinned host memory")
-    host_h, host_b, lay_h = [], [], None
+    log("[bench] encoding the 13-bit history and copying everything to pinned host memory")
+    host_h, host_b, host_l, lay_h, lay_l = [], [], [], None, []
+    n_slots = layers[0]["k_pool"].shape[0]
+    sz = B.l13_sizes(dims, n_slots)
+    l13_arena = torch.empty(sz["arena_bytes"], dtype=torch.uint8, device=device)
+    l13_desc = torch.empty(sz["desc"], dtype=torch.int32, device=device)
+    l13_table = torch.empty(sz["table"], dtype=torch.uint8, device=device)
+    l13_end = torch.empty(1, dtype=torch.int64, device=device)
+    all_slots = torch.arange(n_slots, dtype=torch.int32, device=device)
     for L in layers:
         blk, lay_h = packed([L[k] for k in ("k_codes", "v_codes", "k_chan", "k_tok", "v_chan")]
                             + [L["k_pool"][widx], L["v_pool"][widx]])
         host_h.append([blk])
         host_b.append([pinned(L["k_pool"]), pinned(L["v_pool"])])
+        B.akv_l13_encode_pages(dims, n_slots, L["k_pool"], L["v_pool"], all_slots, all_slots, l13_arena, 0,
+                               l13_desc, l13_table, l13_end)
+        end = int(l13_end[0])
+        blk, lay = packed([l13_arena[:end], l13_desc, l13_table])
+        host_l.append([blk])
+        lay_l.append(lay)
         for k in ("k_codes", "v_codes", "k_chan", "k_tok", "v_chan", "k_pool", "v_pool"):
             del L[k]
+    del l13_arena
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
 
@@ -319,8 +382,12 @@ def run_staged(args, w):
 
     bytes_h = sum(torch.Size(shp).numel() * torch.empty((), dtype=dt).element_size() for _, dt, shp in lay_h) * w.layers
     bytes_b = sum(t.numel() * t.element_size() for t in host_b[0]) * w.layers
+    bytes_l = sum(sum(torch.Size(shp).numel() * torch.empty((), dtype=dt).element_size() for _, dt, shp in lay)
+                  for lay in lay_l)
     ring_h = B.Ring([torch.empty(nbytes(host_h[0]), dtype=torch.uint8, device=device) for _ in range(2)])
     ring_b = B.Ring([torch.empty(nbytes(host_b[0]), dtype=torch.uint8, device=device) for _ in range(2)])
+    ring_l = B.Ring([torch.empty(max(nbytes(h) for h in host_l), dtype=torch.uint8, device=device)
+                     for _ in range(2)])
     copy_s = torch.cuda.Stream()
     comp = torch.cuda.current_stream()
     out = torch.empty((w.batch, w.num_q_heads, w.head_dim), device=device)
@@ -344,6 +411,15 @@ def run_staged(args, w):
             B.akv_decode_attn_exact(dims, w.batch, L["q"], v[0], v[1], T["tf"], T["nf"], mf, sigma, out, outl,
                                     wsb, comp)
             ring_b.release(i, comp)
+
+    def l13_step():
+        for i, L in enumerate(layers):
+            slot = ring_l.stage_views(i, host_l[i], copy_s, comp)[0]
+            v = [slot[o:o + torch.Size(shp).numel() * torch.empty((), dtype=dt).element_size()].view(dt).view(shp)
+                 for o, dt, shp in lay_l[i]]
+            B.akv_decode_attn_l13(dims, w.batch, L["q"], v[0], v[1], v[2], T["tf"], T["nf"], mf, sigma, out, outl,
+                                  wsb, comp)
+            ring_l.release(i, comp)
 
     def timed(fn, steps, warmup):
         for _ in range(warmup):
@@ -377,9 +453,13 @@ def run_staged(args, w):
     ms_h = timed(hybrid_step, steps, 1)
     log("[bench] staged all-BF16 step")
     ms_b = timed(bf16_step, steps, 1)
+    log("[bench] staged lossless 13-bit step")
+    ms_l = timed(l13_step, steps, 1)
     ring_h.destroy()
     ring_b.destroy()
-    return dict(ms_h=ms_h, ms_b=ms_b, bytes_h=bytes_h, bytes_b=bytes_b, h2d_gbps=h2d_gbps, steps=steps)
+    ring_l.destroy()
+    return dict(ms_h=ms_h, ms_b=ms_b, ms_l=ms_l, bytes_h=bytes_h, bytes_b=bytes_b, bytes_l=bytes_l,
+                h2d_gbps=h2d_gbps, steps=steps)
 
 
 def pcie_curve(sizes_mib=(0.0625, 0.25, 1, 4, 16, 64, 256, 512)):
@@ -420,12 +500,17 @@ def staged_sweep(args):
         w = inputs.Workload(f"staged{L // 1024}k", 4, batch=1, layers=16, num_kv_heads=4, group=6, lengths=(L,),
                             window=1024, outlier_frac=0.02, permute=False)
         r = run_staged(args, w)
+        times = {"hybrid": r["ms_h"], "exact": r["ms_b"], "lossless13": r["ms_l"]}
         rows.append(dict(context=L, ms_hybrid=round(r["ms_h"], 3), ms_bf16=round(r["ms_b"], 3),
-                         bytes_hybrid=r["bytes_h"], bytes_bf16=r["bytes_b"],
+                         ms_lossless13=round(r["ms_l"], 3),
+                         bytes_hybrid=r["bytes_h"], bytes_bf16=r["bytes_b"], bytes_lossless13=r["bytes_l"],
                          pcie_GBps_hybrid=round(r["bytes_h"] / (r["ms_h"] * 1e-3) / 1e9, 1),
                          pcie_GBps_bf16=round(r["bytes_b"] / (r["ms_b"] * 1e-3) / 1e9, 1),
-                         chosen="hybrid" if r["ms_h"] < r["ms_b"] else "exact"))
-        log(f"[bench] {w.name}: hybrid {r['ms_h']:.2f} ms, exact {r['ms_b']:.2f} ms")
+                         pcie_GBps_lossless13=round(r["bytes_l"] / (r["ms_l"] * 1e-3) / 1e9, 1),
+                         chosen=min(times, key=times.get),
+                         chosen_lossless_only="lossless13" if r["ms_l"] < r["ms_b"] else "exact"))
+        log(f"[bench] {w.name}: hybrid {r['ms_h']:.2f} ms, exact {r['ms_b']:.2f} ms, "
+            f"lossless13 {r['ms_l']:.2f} ms")
         gc.collect()
         torch.cuda.empty_cache()
     return rows
@@ -560,7 +645,8 @@ def main():
     if args.workload == "staged-sweep":
         curve = pcie_curve()
         rows = staged_sweep(args)
-        print(json.dumps({"metric": "host-staged ms/token vs context, exact vs hybrid (the tier gate)",
+        print(json.dumps({"metric": "host-staged ms/token vs context, exact vs lossless 13-bit vs hybrid "
+                                    "(the tier gate)",
                           "unit": "ms/token", "n_gpus": 1, "higher_is_better": False,
                           "data": "synthetic (the ctx128k recipe at each context length, pinned host history)",
                           "pcie_h2d_curve_MiB_GBps": [[m, round(g, 2)] for m, g in curve],
@@ -584,7 +670,11 @@ def main():
                       "bytes_not_moved_per_token": r["bytes_b"] - r["bytes_h"],
                       "ms_per_token_bf16_staged": round(r["ms_b"], 3),
                       "bf16_staged_GBps": round(r["bytes_b"] / (r["ms_b"] * 1e-3) / 1e9, 1),
-                      "speedup_vs_bf16_staged": round(r["ms_b"] / r["ms_h"], 3)},
+                      "speedup_vs_bf16_staged": round(r["ms_b"] / r["ms_h"], 3),
+                      "lossless13_bytes_staged_per_token": r["bytes_l"],
+                      "ms_per_token_lossless13_staged": round(r["ms_l"], 3),
+                      "lossless13_staged_GBps": round(r["bytes_l"] / (r["ms_l"] * 1e-3) / 1e9, 1),
+                      "lossless13_speedup_vs_bf16_staged": round(r["ms_b"] / r["ms_l"], 3)},
         }), flush=True)
         return
     r = run_gpu(args, w)
@@ -632,6 +722,19 @@ def main():
             "hybrid_speedup_vs_bf16": round(r["ms_bf16"] / ms, 3),
             "quantize_ms_per_layer": round(r["quant_ms_per_layer"], 3),
             "quantize_GBps_read_plus_write": round(r["quant_gbps"], 1),
+            "lossless13": {
+                "us_per_step": round(r["lossless"]["ms_step"] * 1e3, 2),
+                "split_kernel_us": round(r["lossless"]["launch_us"], 2),
+                "bytes_per_launch": r["lossless"]["bytes_per_launch"],
+                "split_kernel_GBps": round(r["lossless"]["bytes_per_launch"] / (r["lossless"]["launch_us"] * 1e-6)
+                                           / 1e9, 1),
+                "arena_bytes_per_layer": r["lossless"]["arena_bytes_per_layer"],
+                "arena_frac_of_bf16": round(r["lossless"]["arena_frac_of_bf16"], 4),
+                "raw_planes": r["lossless"]["raw_planes"], "planes": r["lossless"]["planes"],
+                "encode_ms_per_layer": round(r["lossless"]["encode_ms_per_layer"], 3),
+                "encode_GBps_bf16_in": round(r["lossless"]["encode_GBps_in"], 1),
+                "speedup_vs_bf16": round(r["ms_bf16"] / r["lossless"]["ms_step"], 3),
+            },
         },
     }
     if r["owners"]:
