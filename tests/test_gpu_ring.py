@@ -142,3 +142,55 @@ def test_ring_lifecycle_errors(B):
         torch.cuda.synchronize()
     finally:
         ring.destroy()
+
+
+def test_ring_staged_13bit_equals_resident(B):
+    """The 13-bit history staged through the ring (packed planes, descriptors
+    and tables in one slot per layer) decodes bit-identically to the same
+    records resident in HBM."""
+    from quantized_paged_kv_akv_amd import inputs as I
+    Hkv, G, n, layers = 2, 3, 6, 4
+    d = B.dims(Hkv, G)
+    seq = [n * 64 - 20, 64 * 3]
+    table = torch.tensor([[0, 1, 2, 3, 4, 5], [5, 3, 1, 0, 0, 0]], dtype=torch.int32, device="cuda")
+    lens = torch.tensor(seq, dtype=torch.int32, device="cuda")
+    recs, qs = [], []
+    for layer in range(layers):
+        kp, vp = I.random_pools(900 + layer, n, Hkv)
+        sz = B.l13_sizes(d, n)
+        arena = torch.empty(sz["arena_bytes"], dtype=torch.uint8, device="cuda")
+        desc = torch.empty(sz["desc"], dtype=torch.int32, device="cuda")
+        tab = torch.empty(sz["table"], dtype=torch.uint8, device="cuda")
+        end = torch.empty(1, dtype=torch.int64, device="cuda")
+        s = torch.arange(n, dtype=torch.int32, device="cuda")
+        B.akv_l13_encode_pages(d, n, dev(kp), dev(vp), s, s, arena, 0, desc, tab, end)
+        torch.cuda.synchronize()
+        recs.append((arena[:int(end[0])].clone(), desc, tab))
+        qs.append(dev(I.random_queries(950 + layer, 2, Hkv * G)))
+    ws = torch.empty(max(16, B.akv_decode_workspace_bytes(d, 2, n)), dtype=torch.uint8, device="cuda")
+    ref = []
+    for (arena, desc, tab), q in zip(recs, qs):
+        o = torch.empty((2, Hkv * G, 256), device="cuda")
+        l = torch.empty((2, Hkv * G), device="cuda")
+        B.akv_decode_attn_l13(d, 2, q, arena, desc, tab, table, lens, n, SIG, o, l, ws)
+        ref.append((o, l))
+    torch.cuda.synchronize()
+    srcs = [[r[0].cpu().pin_memory(), r[1].cpu().pin_memory(), r[2].cpu().pin_memory()] for r in recs]
+    slot_bytes = max(_nbytes(x) for x in srcs)
+    say("case ring 13-bit, 4 layers, 2 slots of", slot_bytes, "bytes")
+    ring = B.Ring([torch.empty(slot_bytes, dtype=torch.uint8, device="cuda") for _ in range(2)])
+    copy_s, comp_s = torch.cuda.Stream(), torch.cuda.current_stream()
+    outs = []
+    try:
+        for i, (x, q) in enumerate(zip(srcs, qs)):
+            arena, desc, tab = ring.stage_views(i, x, copy_s, comp_s)
+            o = torch.full((2, Hkv * G, 256), float("nan"), device="cuda")
+            l = torch.full((2, Hkv * G), float("nan"), device="cuda")
+            B.akv_decode_attn_l13(d, 2, q, arena, desc, tab, table, lens, n, SIG, o, l, ws, comp_s)
+            ring.release(i, comp_s)
+            outs.append((o, l))
+        torch.cuda.synchronize()
+    finally:
+        ring.destroy()
+    for i, ((o, l), (ro, rl)) in enumerate(zip(outs, ref)):
+        assert torch.equal(o, ro) and torch.equal(l, rl), f"layer {i} differs from the resident 13-bit decode"
