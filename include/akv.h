@@ -314,7 +314,8 @@ akv_status akv_tables_advance(int32_t batch, const int32_t *count, const int32_t
  *   AKV_ERR_BUDGET, nothing enqueued, unless arena_offset + n * Hkv * 2 *
  *   32,768 <= arena_bytes (room even if every plane is raw); offsets must
  *   stay below 256 GiB.  *arena_end (device int64, 8-byte aligned) receives
- *   the byte offset just past the last plane (arena_offset when n = 0): the
+ *   the byte offset just past the last plane (arena_offset when n = 0; then
+ *   only arena_end is used and the other pointers may be NULL): the
  *   arena_offset of a following call, and the byte count to stage.  Three
  *   kernels on `stream`; src_slot and dst_slot are device int32 arrays.
  *   Errors: AKV_ERR_ARG, AKV_ERR_UNSUPPORTED, AKV_ERR_ALIGN, AKV_ERR_BUDGET.

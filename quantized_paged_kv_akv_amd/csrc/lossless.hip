@@ -232,10 +232,12 @@ extern "C" akv_status akv_l13_encode_pages(const akv_dims* dims, int32_t n, cons
     clear_error();
     akv_status st = check_l13_common(dims, n);
     if (st != AKV_OK) return st;
-    if (!k_bf16 || !v_bf16 || !src_slot || !dst_slot || !l13_arena || !l13_desc || !l13_table || !arena_end)
+    if (!arena_end) return fail(AKV_ERR_ARG, "NULL arena_end");
+    if (n > 0 && (!k_bf16 || !v_bf16 || !src_slot || !dst_slot || !l13_arena || !l13_desc || !l13_table))
         return fail(AKV_ERR_ARG, "NULL pointer");
-    if (!aligned16(k_bf16) || !aligned16(v_bf16) || !aligned16(l13_table) || !aligned(l13_arena, 256) ||
-        !aligned(l13_desc, 4) || !aligned(src_slot, 4) || !aligned(dst_slot, 4) || !aligned(arena_end, 8))
+    if (!aligned(arena_end, 8) ||
+        (n > 0 && (!aligned16(k_bf16) || !aligned16(v_bf16) || !aligned16(l13_table) || !aligned(l13_arena, 256) ||
+                   !aligned(l13_desc, 4) || !aligned(src_slot, 4) || !aligned(dst_slot, 4))))
         return fail(AKV_ERR_ALIGN, "pointer alignment (tensors 16, arena 256, int32 arrays 4, arena_end 8 bytes)");
     if (arena_offset < 0 || arena_offset % 256 != 0 || arena_bytes < arena_offset)
         return fail(AKV_ERR_ARG, "arena_offset %lld must be a multiple of 256 in [0, arena_bytes = %lld]",

@@ -85,3 +85,35 @@ def test_workspace_is_deterministic_and_covers_splits(B):
         assert a == B.akv_decode_workspace_bytes(d, batch, mp)
         # at least one partial row per (request, query head)
         assert a >= batch * 24 * (256 + 1) * 4
+
+
+def test_lossless_host_side_validation(B):
+    """The 13-bit entry points refuse bad arguments before any GPU work: an
+    arena too small for the worst case, an unaligned offset or arena, a
+    negative count, a small decode workspace."""
+    lib = B._lib
+    d = B.dims(2, 3)
+    p, a256, end = ctypes.c_void_p(256), ctypes.c_void_p(4096), ctypes.c_void_p(64)
+    worst = 5 * 2 * 2 * 32768
+    # 5 pages x 2 heads x 2 planes: the arena must hold them all raw
+    assert lib.akv_l13_encode_pages(ctypes.byref(d), 5, p, p, p, p, a256, 0, worst - 256, p, p, end, None) == -5
+    assert "raw" in lib.akv_last_error().decode()
+    assert lib.akv_l13_encode_pages(ctypes.byref(d), 5, p, p, p, p, a256, 256, worst, p, p, end, None) == -5
+    assert lib.akv_l13_encode_pages(ctypes.byref(d), 5, p, p, p, p, a256, 100, 10 * worst, p, p, end, None) == -1
+    assert lib.akv_l13_encode_pages(ctypes.byref(d), 5, p, p, p, p, ctypes.c_void_p(4112), 0, worst, p, p, end,
+                                    None) == -3
+    assert lib.akv_l13_encode_pages(ctypes.byref(d), -1, p, p, p, p, a256, 0, worst, p, p, end, None) == -1
+    assert lib.akv_l13_encode_pages(ctypes.byref(d), 5, p, p, p, p, a256, 0, worst, p, p, None, None) == -1
+    bad = B.dims(2, 3, page_size=32)
+    assert lib.akv_l13_encode_pages(ctypes.byref(bad), 5, p, p, p, p, a256, 0, worst, p, p, end, None) == -2
+    assert lib.akv_l13_decode_pages(ctypes.byref(d), 0, None, None, None, None, None, None, None, None) == 0
+    assert lib.akv_l13_decode_pages(ctypes.byref(d), 3, a256, p, p, p, p, p, None, None) == -1
+    # decode: arena alignment and workspace size
+    t4 = ctypes.c_void_p(20)
+    st = lib.akv_decode_attn_l13(ctypes.byref(d), 1, p, ctypes.c_void_p(4112), t4, p, t4, t4, 64, 0.0625, p, p, p,
+                                 1 << 20, None)
+    assert st == -3
+    st = lib.akv_decode_attn_l13(ctypes.byref(d), 1, p, a256, t4, p, t4, t4, 64, 0.0625, p, p, p, 16, None)
+    assert st == -4
+    sz = B.l13_sizes(d, 7)
+    assert sz["desc"] == (7, 2, 2) and sz["table"] == (7, 2, 2, 32) and sz["arena_bytes"] == 7 * 2 * 2 * 32768
