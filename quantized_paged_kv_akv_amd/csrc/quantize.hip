@@ -44,6 +44,18 @@ __device__ __forceinline__ int code_of(double x, double a, double b, double inv_
     return (int)r;
 }
 
+// code_of for a nonzero scale, with fewer operations: the nearest integer
+// of the estimate is the answer unless the estimate lies within 2^-30 of a
+// half-integer, where the correctly rounded quotient decides -- the same
+// decisions as code_of.  (Callers give a zero scale code 0 themselves.)
+__device__ __forceinline__ int code_rint(double x, double a, double b, double inv_ab) {
+    const double q = x * inv_ab;
+    double r = rint(q);
+    if (fabs(fabs(q - r) - 0.5) < 0x1p-30) r = rint(x / (a * b));
+    r = fmin(fmax(r, -127.0), 127.0);
+    return (int)r;
+}
+
 __global__ __launch_bounds__(256) void quantize_kernel(
     int Hkv, const uint16_t* __restrict__ kbf, const uint16_t* __restrict__ vbf,
     const int32_t* __restrict__ src, const int32_t* __restrict__ dst, int8_t* __restrict__ kcodes,
@@ -145,9 +157,13 @@ __global__ __launch_bounds__(256) void quantize_kernel(
     {
         int8_t* out = kcodes + dp * (kP * kD);
         const double cd = (double)c32s[d], icd = invc[d];
+        int8_t* od = out + kcode_offset(0, d);  // kcode_offset(t, d) - kcode_offset(0, d) depends on t only
+#pragma unroll
         for (int t = 0; t < kP; ++t) {
             const double x = (double)bf16_to_f32(Ks[t][d]);
-            out[kcode_offset(t, d)] = (int8_t)code_of(x, cd, (double)s32s[t], icd * invs[t]);
+            // c_d is never zero; a zero token factor (the same for every lane) gives code 0
+            const int keep = __builtin_amdgcn_readfirstlane(__float_as_int(s32s[t])) == 0 ? 0 : -1;
+            od[kcode_offset(t, 0)] = (int8_t)(code_rint(x, cd, (double)s32s[t], icd * invs[t]) & keep);
         }
     }
 
@@ -160,6 +176,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(
             m = fmax(m, fabs((double)bf16_to_f32((uint16_t)(vw[k] >> 16))));
         }
         const float vs32 = (float)(m / 127.0);
+        const int vkeep = vs32 == 0.0f ? 0 : -1;  // a zero value scale gives code 0
         vchan[dp * kD + d] = vs32;
         const double vs = (double)vs32, ivs = vs != 0.0 ? 1.0 / vs : 0.0;
         u32x4* out = reinterpret_cast<u32x4*>(vcodes + dp * (kP * kD) + (size_t)d * kP);
@@ -173,7 +190,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(
                 for (int e = 0; e < 4; ++e) {
                     const int tok = 16 * k + 4 * j + e;
                     const uint16_t b = (tok & 1) ? (uint16_t)(vw[tok >> 1] >> 16) : (uint16_t)(vw[tok >> 1] & 0xFFFFu);
-                    const int cv = code_of((double)bf16_to_f32(b), vs, 1.0, ivs);
+                    const int cv = code_rint((double)bf16_to_f32(b), vs, 1.0, ivs) & vkeep;
                     packed |= ((uint32_t)(cv & 0xFF)) << (8 * e);
                 }
                 wds[j] = packed;
