@@ -7,7 +7,10 @@
 // weights multiply the raw value codes, and the per-channel value scale is
 // applied to the page's PV result at the page boundary.
 // Exact tier ("SYCL" page, "A merge that joins the tiers"): BF16 decode that
-// also returns the log-sum-exp, -inf for an empty range.
+// also returns the log-sum-exp, -inf for an empty range.  The same body
+// reads the lossless 13-bit planes ("Model quantization" page, "A lossless
+// tier first"), expanding each operand register to BF16 right before its
+// MFMA, so its results are bit-identical to the BF16 pages'.
 //
 // Both tiers contract with 16x16x32 MFMAs (FP16 for int8 codes, which become
 // FP16 exactly; BF16 for the exact tier), QK as S^T (tokens x heads) = K Q^T
