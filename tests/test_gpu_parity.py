@@ -50,7 +50,8 @@ def test_quantize_random_pages_outliers(B):
 def _edge_pages():
     """Pages that stress the format: all-zero page, zero channel, zero token,
     constant page, a channel far below the rest (clamp binds), exact ties,
-    huge and tiny magnitudes."""
+    huge and tiny magnitudes, scales beyond 2^+-100 and a token whose |K| / c
+    exceeds the FP32 range."""
     r = np.random.default_rng(5)
     pages_k, pages_v = [], []
 
@@ -74,6 +75,14 @@ def _edge_pages():
     T = np.array([np.roll(row, t % 8) for t in range(64)])
     add(T, T)
     add(base_k * 1e-20, base_v * 1e-30)
+    # scales outside the kernel's FP32 estimate range [2^-100, 2^100]: every
+    # code of such a token or channel goes through the float64 divide
+    add(base_k * 1e-33, base_v * 1e-33)
+    add(base_k * 1e33, base_v * 1e33)
+    # |K| / c beyond the FP32 range although s_t is finite: channel 0 holds
+    # one huge value (so c_0 < 1) while every other channel is huge throughout
+    K = np.full((64, 256), 3.0e38); K[:, 0] = 0.0; K[7, 0] = 3.0e38
+    add(K, base_v)
     kp = np.stack(pages_k)[:, None]
     vp = np.stack(pages_v)[:, None]
     return kp, vp
