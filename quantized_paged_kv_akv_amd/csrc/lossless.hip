@@ -42,33 +42,44 @@ __device__ __forceinline__ void copy_plane(uint8_t* out, const uint8_t* in, int 
     }
 }
 
+// Flag slot of high byte hb in LDS: one dword each, bit 4 of the slot index
+// flipped for negative values so that the high bytes of +x and -x, which
+// differ only in bit 7, sit in different banks.
+__device__ __forceinline__ int flag_slot(uint32_t hb) { return (int)(hb ^ ((hb >> 3) & 16u)); }
+
 // Pass 1, one work-group per plane: the plane's table and raw flag (the flag
-// goes to the descriptor, which pass 2 completes).
+// goes to the descriptor, which pass 2 completes).  Every value stores 1 into
+// its high byte's flag (all writers store the same value, so no atomics);
+// each wave then gathers 64 flags with a ballot.
 __global__ __launch_bounds__(256) void l13_table_kernel(int Hkv, const uint16_t* kb, const uint16_t* vb,
                                                         const int32_t* src, const int32_t* dst, int32_t* desc,
                                                         uint8_t* table) {
     const int i = blockIdx.x, h = blockIdx.y, kv = blockIdx.z;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    __shared__ uint32_t flag[256];
     __shared__ uint32_t present[8];
     __shared__ uint32_t tab[8];
-    if (tid < 8) {
-        present[tid] = 0u;
-        tab[tid] = 0u;
-    }
-    __syncthreads();
+    flag[tid] = 0u;
+    if (tid < 8) tab[tid] = 0u;
     u32x4 x[8];
     plane_load((kv ? vb : kb) + ((size_t)src[i] * Hkv + h) * (kP * kD), kv, w, l, x);
-    uint32_t m[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+    __syncthreads();
 #pragma unroll
-    for (int v = 0; v < 64; ++v) {
-        const uint32_t hb = value_bits(x, v) >> 8;
-        const uint32_t bit = 1u << (hb & 31u);
+    for (int r = 0; r < 8; ++r) {
+        const uint32_t wd[4] = {x[r].x, x[r].y, x[r].z, x[r].w};
 #pragma unroll
-        for (int k = 0; k < 8; ++k) m[k] |= (hb >> 5) == (uint32_t)k ? bit : 0u;
+        for (int e = 0; e < 4; ++e) {
+            flag[flag_slot((wd[e] >> 8) & 0xFFu)] = 1u;
+            flag[flag_slot(wd[e] >> 24)] = 1u;
+        }
     }
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-        if (m[k]) atomicOr(&present[k], m[k]);
+    __syncthreads();
+    // wave w gathers high bytes 64 w .. 64 w + 63
+    const unsigned long long bits = __ballot(flag[flag_slot((uint32_t)tid)] != 0u);
+    if (l == 0) {
+        present[2 * w] = (uint32_t)bits;
+        present[2 * w + 1] = (uint32_t)(bits >> 32);
+    }
     __syncthreads();
     // thread tid stands for high byte tid: its table position is the number of present bytes below it
     int count = 0, below = 0;
