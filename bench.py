@@ -281,7 +281,7 @@ def run_gpu(args, w):
     def pct(q):
         return step_us[min(len(step_us) - 1, int(q * (len(step_us) - 1) + 0.5))]
 
-    # streaming-read ceiling of this GPU: a plain 16-byte-load read of 4 GiB
+    # streaming-read ceiling of this GPU: a non-temporal 16-byte-load read of 4 GiB
     log("[bench] streaming-read ceiling")
     big = torch.ones(4 << 30, dtype=torch.uint8, device=device)
     sink = torch.zeros(1, dtype=torch.int32, device=device)

@@ -107,8 +107,8 @@ akv_status akv_set_profile_events(void *start_event, void *stop_event);
 
 /*
  * Instrumentation: one plain streaming read of `bytes` (a multiple of 16 at
- * least 32 KiB) of device memory at `buf` (16-byte aligned) with 16-byte
- * vector loads from 2048 work-groups, the streaming-read ceiling the decode
+ * least 32 KiB) of device memory at `buf` (16-byte aligned) with non-temporal
+ * 16-byte vector loads from 2048 work-groups, the streaming-read ceiling the decode
  * kernels' HBM rate is reported against.  Reads floor(bytes / 32 KiB) * 32 KiB
  * bytes; `sink` is a device word that is written only on an impossible value.
  * Errors: AKV_ERR_ARG, AKV_ERR_ALIGN.
