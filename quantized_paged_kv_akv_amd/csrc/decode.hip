@@ -15,7 +15,9 @@
 // Both tiers contract with 16x16x32 MFMAs (FP16 for int8 codes, which become
 // FP16 exactly; BF16 for the exact tier), QK as S^T (tokens x heads) = K Q^T
 // and PV as O^T (channels x heads) = V^T P^T, with V stored channel-major so
-// a lane's 16-byte load is one PV operand.  The 16 MFMA columns carry each
+// 16 bytes of a value row are one PV operand (int8 tiles are loaded straight
+// into operand registers; BF16 pages are loaded in whole lines and their
+// operands rebuilt through LDS, see Bf16Source).  The 16 MFMA columns carry each
 // query head twice, so an FP32 operand (q' for the int8 tier, the softmax
 // weights P for both) is fed as a high and a low half-precision part in one
 // MFMA and the two halves of the result are added afterwards.
@@ -79,6 +81,12 @@ struct ExactArgs {
 // LDS of the exact tier's body
 struct ExactSmem {
     float part[2][4][16][64];  // QK partial logits of the four waves, double-buffered
+};
+
+// LDS of the BF16 operand source: per wave, its 64-channel quarter of a page's
+// K, then of its V (64 rows of eight 16-byte pieces)
+struct Bf16Stage {
+    u32x4 q[4][512];
 };
 
 // Sum the four waves' partial logits for this lane: tile t, row r is token
@@ -455,26 +463,68 @@ __device__ __forceinline__ u32x4 mask_tokens(u32x4 v, int first, int limit) {
 // registers for this lane (the next page's while the current one is in
 // use); keys() and values() hand the eight BF16 operand registers, in
 // order, to f.
-struct Bf16Source {  // the BF16 pool: the loaded registers are the operands
+// The BF16 pool.  Loads are issued in whole 128-byte lines (register i of
+// lane l is piece l % 8 of row 8 i + l / 8 of the wave's quarter: K token
+// rows, V channel rows), non-temporal, and the MFMA operands are rebuilt
+// through the wave's LDS quarter page: the operand layout alone would give
+// each load instruction half lines, which streams about 12% slower.  Piece p
+// of row x is stored at 8 x + (p ^ swizzle(x)), so the operand reads of eight
+// lanes fall in eight different bank groups.
+struct Bf16Source {
     const uint16_t* kb;
     const uint16_t* vb;
+    u32x4* stage;  // this wave's LDS quarter page (512 pieces)
     struct Page {
         u32x4 k[8], v[8];
     };
     __device__ __forceinline__ void load(int slot, int kvh, int Hkv, int w, int l, Page& R) const {
         const size_t base = ((size_t)slot * Hkv + kvh) * (kP * kD);
-        bf16_keys_load(kb + base, w, l & 15, l >> 4, R.k);
-        bf16_values_load(vb + base, w, l & 15, l >> 4, R.v);
+        const uint16_t* kp = kb + base + (l >> 3) * kD + 64 * w + 8 * (l & 7);
+        const uint16_t* vp = vb + base + (64 * w + (l >> 3)) * kP + 8 * (l & 7);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            R.k[i] = ld16_stream(kp + 8 * i * kD);
+            R.v[i] = ld16_stream(vp + 8 * i * kP);
+        }
     }
+    // Key register 2t + s of lane (n, g) is token qk_row_token(t, n),
+    // channels 64 w + 16 g + 8 s .. + 8 (piece 2 g + s); key rows swizzle by
+    // (T & 3) | (T >> 2 & 4), which is n & 7 for the rows a lane reads.
+    // The wave's LDS operations run in program order; the empty asm statements
+    // keep the compiler from moving them across each other.
     template <class F>
     __device__ __forceinline__ void keys(const Page& R, F&& f) const {
+        const int l = threadIdx.x & 63, n = l & 15, g = l >> 4;
+        asm volatile("" ::: "memory");
 #pragma unroll
-        for (int r = 0; r < 8; ++r) f(r, R.k[r]);
+        for (int i = 0; i < 8; ++i) {
+            const int T = 8 * i + (l >> 3);
+            stage[8 * T + ((l & 7) ^ ((T & 3) | ((T >> 2) & 4)))] = R.k[i];
+        }
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const int T = qk_row_token(r >> 1, n);
+            f(r, stage[8 * T + ((2 * g + (r & 1)) ^ (n & 7))]);
+        }
     }
+    // Value register 2j + s of lane (n, g) is channel 64 w + 16 j + n, tokens
+    // 16 g + 8 s .. + 8 (piece 2 g + s); value rows swizzle by c & 7.
     template <class F>
     __device__ __forceinline__ void values(const Page& R, F&& f) const {
+        const int l = threadIdx.x & 63, n = l & 15, g = l >> 4;
+        asm volatile("" ::: "memory");
 #pragma unroll
-        for (int r = 0; r < 8; ++r) f(r, R.v[r]);
+        for (int i = 0; i < 8; ++i) {
+            const int c = 8 * i + (l >> 3);
+            stage[8 * c + ((l & 7) ^ (c & 7))] = R.v[i];
+        }
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const int c = 16 * (r >> 1) + n;
+            f(r, stage[8 * c + ((2 * g + (r & 1)) ^ (c & 7))]);
+        }
     }
 };
 
@@ -635,7 +685,10 @@ __device__ __forceinline__ void exact_split(const ExactArgs& a, const Src& src, 
 
 union SplitSmem {
     Int8Smem i8;
-    ExactSmem ex;
+    struct {
+        ExactSmem ex;
+        Bf16Stage st;
+    } bx;
 };
 
 __global__ __launch_bounds__(kThreads, 2) void decode_int8_kernel(Int8Args a) {
@@ -645,7 +698,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_int8_kernel(Int8Args a) {
 
 __global__ __launch_bounds__(kThreads, 2) void decode_exact_kernel(ExactArgs a) {
     __shared__ ExactSmem sm;
-    exact_split(a, Bf16Source{a.kb, a.vb}, sm, blockIdx.x, blockIdx.y, blockIdx.z);
+    __shared__ Bf16Stage st;
+    exact_split(a, Bf16Source{a.kb, a.vb, st.q[threadIdx.x >> 6]}, sm, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 // The exact body over lossless 13-bit planes: same split plan and
@@ -663,7 +717,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_l13_kernel(ExactArgs a, L1
 __global__ __launch_bounds__(kThreads, 2) void decode_hybrid_kernel(Int8Args a8, ExactArgs ax, int nw) {
     __shared__ SplitSmem sm;
     if ((int)blockIdx.x < nw)
-        exact_split(ax, Bf16Source{ax.kb, ax.vb}, sm.ex, blockIdx.x, blockIdx.y, blockIdx.z);
+        exact_split(ax, Bf16Source{ax.kb, ax.vb, sm.bx.st.q[threadIdx.x >> 6]}, sm.bx.ex, blockIdx.x, blockIdx.y, blockIdx.z);
     else
         int8_split(a8, sm.i8, blockIdx.x - nw, blockIdx.y, blockIdx.z);
 }
