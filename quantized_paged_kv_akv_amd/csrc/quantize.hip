@@ -89,26 +89,41 @@ __global__ __launch_bounds__(256) void quantize_kernel(
     __shared__ int red_cnt[4];
     const uint16_t* Ks16 = reinterpret_cast<const uint16_t*>(Ks4);
 
-    // value rows first (thread d owns channel row d: 64 contiguous tokens)
+    // Both pages are read as whole lines (each load instruction covers 1 KB
+    // contiguous), non-temporal: the value page goes through LDS to give
+    // thread d its channel row d (64 tokens, 128 bytes; piece k of row d at
+    // d * 8 + (k ^ (d & 7)), so eight neighbouring rows spread over eight
+    // bank groups), then the key page takes the same LDS.
+    u32x4 kin[(kP * kD * 2) / (16 * 256)];
     uint32_t vw[32];
     {
-        const u32x4* row = reinterpret_cast<const u32x4*>(V + (size_t)tid * kP);
+        const u32x4* v4 = reinterpret_cast<const u32x4*>(V);
+        const u32x4* k4 = reinterpret_cast<const u32x4*>(K);
+        u32x4 vin[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) vin[k] = __builtin_nontemporal_load(v4 + tid + 256 * k);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) kin[k] = __builtin_nontemporal_load(k4 + tid + 256 * k);
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            const u32x4 x = row[k];
+            const int c = tid + 256 * k, row = c >> 3;
+            Ks4[row * 8 + ((c & 7) ^ (row & 7))] = vin[k];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const u32x4 x = Ks4[tid * 8 + (k ^ (tid & 7))];
             vw[4 * k + 0] = x.x;
             vw[4 * k + 1] = x.y;
             vw[4 * k + 2] = x.z;
             vw[4 * k + 3] = x.w;
         }
-    }
-    // the key page (32 KB) into LDS with coalesced 16-byte loads
-    {
-        const u32x4* src4 = reinterpret_cast<const u32x4*>(K);
+        __syncthreads();
+        // the key page, token rows of 32 chunks, chunk c of row t at c ^ ksw(t)
 #pragma unroll
-        for (int k = 0; k < (kP * kD * 2) / (16 * 256); ++k) {
+        for (int k = 0; k < 8; ++k) {
             const int c = tid + 256 * k, row = c >> 5;
-            Ks4[row * 32 + ((c & 31) ^ ksw(row))] = src4[c];
+            Ks4[row * 32 + ((c & 31) ^ ksw(row))] = kin[k];
         }
     }
 
