@@ -137,23 +137,11 @@ __device__ __forceinline__ void split_bf16(float x, __bf16& hi, __bf16& lo) {
 // 16 (i / 4) + 4 t + i % 4 of the page.
 __host__ __device__ __forceinline__ int qk_row_token(int t, int i) { return 16 * (i >> 2) + 4 * t + (i & 3); }
 
-// BF16 page-head loads of lane (w, n, g): key register 2t + s is token
-// qk_row_token(t, n) at channels 64w + 16g + 8s .. + 8; value register 2j + s
-// is channel 64w + 16j + n at tokens 16g + 8s .. + 8.
-__device__ __forceinline__ void bf16_keys_load(const uint16_t* kp, int w, int n, int g, u32x4 (&K)[8]) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int s = 0; s < 2; ++s) K[2 * t + s] = ld16(kp + qk_row_token(t, n) * kD + 64 * w + 16 * g + 8 * s);
-}
-__device__ __forceinline__ void bf16_values_load(const uint16_t* vp, int w, int n, int g, u32x4 (&V)[8]) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int s = 0; s < 2; ++s) V[2 * j + s] = ld16(vp + (64 * w + 16 * j + n) * kP + 16 * g + 8 * s);
-}
-
-// BF16 stores mirroring the loads above.
+// Lane-slot order of a BF16 page-head (the exact body's MFMA operands, and
+// the order in which 13-bit planes are stored): register 2t + s of lane
+// (w, n, g) holds key token qk_row_token(t, n) at channels 64w + 16g + 8s .. + 8;
+// register 2j + s holds value channel 64w + 16j + n at tokens 16g + 8s .. + 8.
+// These stores write a lane's registers to a BF16 page-head in that order.
 __device__ __forceinline__ void bf16_keys_store(uint16_t* kp, int w, int n, int g, const u32x4 (&K)[8]) {
 #pragma unroll
     for (int t = 0; t < 4; ++t)

@@ -17,15 +17,8 @@ namespace akv {
 constexpr int kL13Units = kL13PlaneBytes / 256;  // 104 arena units of 256 bytes
 constexpr int kL13RawUnits = kL13RawBytes / 256;  // 128
 
-// lane (w, l)'s 64 values of a BF16 plane (keys kv = 0, values kv = 1) in
-// lane-slot order: register r holds values 8r .. 8r + 7.
-__device__ __forceinline__ void plane_load(const uint16_t* p, int kv, int w, int l, u32x4 (&x)[8]) {
-    if (kv == 0)
-        bf16_keys_load(p, w, l & 15, l >> 4, x);
-    else
-        bf16_values_load(p, w, l & 15, l >> 4, x);
-}
-
+// BF16 value v (0..63) of a lane's eight 16-byte registers in lane-slot
+// order (register v / 8).
 __device__ __forceinline__ uint16_t value_bits(const u32x4 (&x)[8], int v) {
     const u32x4 r = x[v >> 3];
     const int c = (v >> 1) & 3;
@@ -61,8 +54,14 @@ __global__ __launch_bounds__(256) void l13_table_kernel(int Hkv, const uint16_t*
     __shared__ uint32_t tab[8];
     flag[tid] = 0u;
     if (tid < 8) tab[tid] = 0u;
+    // the set of high bytes does not depend on which thread reads which value:
+    // read the plane as whole lines, non-temporal
     u32x4 x[8];
-    plane_load((kv ? vb : kb) + ((size_t)src[i] * Hkv + h) * (kP * kD), kv, w, l, x);
+    {
+        const u32x4* p4 = reinterpret_cast<const u32x4*>((kv ? vb : kb) + ((size_t)src[i] * Hkv + h) * (kP * kD));
+#pragma unroll
+        for (int k = 0; k < 8; ++k) x[k] = __builtin_nontemporal_load(p4 + tid + 256 * k);
+    }
     __syncthreads();
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
@@ -160,13 +159,47 @@ __global__ __launch_bounds__(256) void l13_encode_kernel(int Hkv, const uint16_t
         return;
     }
     __shared__ uint8_t pos[256];
+    __shared__ u32x4 stage[kP * kD / 8];
     if (tid < 32) {
         const uint8_t e = table[plane * 32 + tid];
         if (tid == 0 || e != 0) pos[e] = (uint8_t)tid;  // entries past the distinct count are 0
     }
+    // The plane is read as whole lines (non-temporal) into LDS, then every lane
+    // takes its values in the decode kernel's load order from there.  Rows of
+    // 16-byte chunks are XOR-swizzled so the lane-order reads spread over the
+    // banks: key rows (64 tokens x 32 chunks) by (t & 3) | (t >> 2 & 4),
+    // value rows (256 channels x 8 chunks) by c & 7.
+    {
+        const u32x4* p4 = reinterpret_cast<const u32x4*>(in);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int c = tid + 256 * k;
+            const u32x4 v = __builtin_nontemporal_load(p4 + c);
+            if (kv == 0) {
+                const int t = c >> 5;
+                stage[t * 32 + ((c & 31) ^ ((t & 3) | ((t >> 2) & 4)))] = v;
+            } else {
+                const int ch = c >> 3;
+                stage[ch * 8 + ((c & 7) ^ (ch & 7))] = v;
+            }
+        }
+    }
     __syncthreads();
     u32x4 x[8];
-    plane_load(in, kv, w, l, x);
+    {
+        const int n = l & 15, g = l >> 4;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const int s2 = r & 1;
+            if (kv == 0) {  // register 2t + s: token qk_row_token(t, n), channels 64 w + 16 g + 8 s
+                const int t = qk_row_token(r >> 1, n);
+                x[r] = stage[t * 32 + ((8 * w + 2 * g + s2) ^ ((t & 3) | ((t >> 2) & 4)))];
+            } else {        // register 2j + s: channel 64 w + 16 j + n, tokens 16 g + 8 s
+                const int ch = 64 * w + 16 * (r >> 1) + n;
+                x[r] = stage[ch * 8 + ((2 * g + s2) ^ (ch & 7))];
+            }
+        }
+    }
     uint32_t lowb[16], nib[8], hib[2] = {0u, 0u};
 #pragma unroll
     for (int k = 0; k < 16; ++k) lowb[k] = 0u;
