@@ -159,45 +159,22 @@ __global__ __launch_bounds__(256) void l13_encode_kernel(int Hkv, const uint16_t
         return;
     }
     __shared__ uint8_t pos[256];
-    __shared__ u32x4 stage[kP * kD / 8];
     if (tid < 32) {
         const uint8_t e = table[plane * 32 + tid];
         if (tid == 0 || e != 0) pos[e] = (uint8_t)tid;  // entries past the distinct count are 0
     }
-    // The plane is read as whole lines (non-temporal) into LDS, then every lane
-    // takes its values in the decode kernel's load order from there.  Rows of
-    // 16-byte chunks are XOR-swizzled so the lane-order reads spread over the
-    // banks: key rows (64 tokens x 32 chunks) by (t & 3) | (t >> 2 & 4),
-    // value rows (256 channels x 8 chunks) by c & 7.
-    {
-        const u32x4* p4 = reinterpret_cast<const u32x4*>(in);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int c = tid + 256 * k;
-            const u32x4 v = __builtin_nontemporal_load(p4 + c);
-            if (kv == 0) {
-                const int t = c >> 5;
-                stage[t * 32 + ((c & 31) ^ ((t & 3) | ((t >> 2) & 4)))] = v;
-            } else {
-                const int ch = c >> 3;
-                stage[ch * 8 + ((c & 7) ^ (ch & 7))] = v;
-            }
-        }
-    }
     __syncthreads();
+    // the lane's values in lane-slot order, loaded straight into registers (an
+    // LDS copy read as whole lines ran this pass slower: 206 against 173 us
+    // per 128K layer)
     u32x4 x[8];
     {
         const int n = l & 15, g = l >> 4;
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
             const int s2 = r & 1;
-            if (kv == 0) {  // register 2t + s: token qk_row_token(t, n), channels 64 w + 16 g + 8 s
-                const int t = qk_row_token(r >> 1, n);
-                x[r] = stage[t * 32 + ((8 * w + 2 * g + s2) ^ ((t & 3) | ((t >> 2) & 4)))];
-            } else {        // register 2j + s: channel 64 w + 16 j + n, tokens 16 g + 8 s
-                const int ch = 64 * w + 16 * (r >> 1) + n;
-                x[r] = stage[ch * 8 + ((2 * g + s2) ^ (ch & 7))];
-            }
+            x[r] = kv == 0 ? ld16(in + qk_row_token(r >> 1, n) * kD + 64 * w + 16 * g + 8 * s2)
+                           : ld16(in + (64 * w + 16 * (r >> 1) + n) * kP + 16 * g + 8 * s2);
         }
     }
     uint32_t lowb[16], nib[8], hib[2] = {0u, 0u};
