@@ -170,11 +170,12 @@ __global__ __launch_bounds__(256) void l13_encode_kernel(int Hkv, const uint16_t
     u32x4 x[8];
     {
         const int n = l & 15, g = l >> 4;
+        if (kv == 0) {
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const int s2 = r & 1;
-            x[r] = kv == 0 ? ld16(in + qk_row_token(r >> 1, n) * kD + 64 * w + 16 * g + 8 * s2)
-                           : ld16(in + (64 * w + 16 * (r >> 1) + n) * kP + 16 * g + 8 * s2);
+            for (int r = 0; r < 8; ++r) x[r] = ld16(in + qk_row_token(r >> 1, n) * kD + 64 * w + 16 * g + 8 * (r & 1));
+        } else {
+#pragma unroll
+            for (int r = 0; r < 8; ++r) x[r] = ld16(in + (64 * w + 16 * (r >> 1) + n) * kP + 16 * g + 8 * (r & 1));
         }
     }
     uint32_t lowb[16], nib[8], hib[2] = {0u, 0u};
