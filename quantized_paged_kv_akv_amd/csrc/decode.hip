@@ -490,8 +490,9 @@ struct Bf16Source {
     // Key register 2t + s of lane (n, g) is token qk_row_token(t, n),
     // channels 64 w + 16 g + 8 s .. + 8 (piece 2 g + s); key rows swizzle by
     // (T & 3) | (T >> 2 & 4), which is n & 7 for the rows a lane reads.
-    // The wave's LDS operations run in program order; the empty asm statements
-    // keep the compiler from moving them across each other.
+    // Before reading pieces that other lanes wrote, the wave waits for its LDS
+    // writes to complete (lgkmcnt 0); the empty asm statements keep the
+    // compiler from moving LDS accesses across those points.
     template <class F>
     __device__ __forceinline__ void keys(const Page& R, F&& f) const {
         const int l = threadIdx.x & 63, n = l & 15, g = l >> 4;
@@ -501,12 +502,16 @@ struct Bf16Source {
             const int T = 8 * i + (l >> 3);
             stage[8 * T + ((l & 7) ^ ((T & 3) | ((T >> 2) & 4)))] = R.k[i];
         }
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
         asm volatile("" ::: "memory");
+        u32x4 op[8];
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
             const int T = qk_row_token(r >> 1, n);
-            f(r, stage[8 * T + ((2 * g + (r & 1)) ^ (n & 7))]);
+            op[r] = stage[8 * T + ((2 * g + (r & 1)) ^ (n & 7))];
         }
+#pragma unroll
+        for (int r = 0; r < 8; ++r) f(r, op[r]);
     }
     // Value register 2j + s of lane (n, g) is channel 64 w + 16 j + n, tokens
     // 16 g + 8 s .. + 8 (piece 2 g + s); value rows swizzle by c & 7.
@@ -519,12 +524,16 @@ struct Bf16Source {
             const int c = 8 * i + (l >> 3);
             stage[8 * c + ((l & 7) ^ (c & 7))] = R.v[i];
         }
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
         asm volatile("" ::: "memory");
+        u32x4 op[8];
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
             const int c = 16 * (r >> 1) + n;
-            f(r, stage[8 * c + ((2 * g + (r & 1)) ^ (c & 7))]);
+            op[r] = stage[8 * c + ((2 * g + (r & 1)) ^ (c & 7))];
         }
+#pragma unroll
+        for (int r = 0; r < 8; ++r) f(r, op[r]);
     }
 };
 
