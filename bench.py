@@ -563,6 +563,12 @@ def cpu_baseline(w):
     rows = units * w.group
     O.merge(np.stack([o8.reshape(rows, 256), ow.reshape(rows, 256)]), np.stack([l8.reshape(rows), lw.reshape(rows)]))
     wall = time.time() - t0
+    # one unit alone: the oracle's parallel loop then runs it on one thread
+    t1 = time.time()
+    O.decode_int8(q[:1], qz["k_codes"], qz["v_codes"], qz["k_chan"], qz["k_tok"], qz["v_chan"], t8[:1], n8[:1], 1,
+                  w.group, configs.SIGMA, mode=1)
+    O.decode_exact(q[:1], d["k_pool"], d["v_pool"], tw[:1], nw[:1], 1, w.group, configs.SIGMA)
+    unit_1t = time.time() - t1
     per_step_units = w.batch * w.layers * w.num_kv_heads
     us_per_step = wall * 1e6 * per_step_units / units
     threads = min(O.num_threads(), units)
@@ -579,7 +585,8 @@ def cpu_baseline(w):
                        f"({plan.n8[0]} int8 pages + {plan.win_tokens[0]}-token window each), "
                        f"float64, {wall:.1f}s wall on {threads} threads of {cpu}, "
                        f"scaled x{per_step_units / units:g} to one 16-layer step",
-                wall_s=wall)
+                wall_s=wall, single_thread_unit_ms=unit_1t * 1e3,
+                single_thread_layer_ms=unit_1t * 1e3 * w.batch * w.num_kv_heads)
 
 
 def profile_kernels(args, w):
