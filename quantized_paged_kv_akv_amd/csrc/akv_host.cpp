@@ -59,15 +59,17 @@ SplitPlan plan_splits(const akv_dims* d, int batch, int max_pages) {
 }
 
 // Two waves per SIMD are resident (2048 on the chip); give each about an equal
-// share of the page-heads, at least 3 pages so the per-wave set-up, the first
-// page's latency and the end-of-split merge stay small (measured at 32K: 3
-// pages per wave beat 2 by a fifth).  A work-group is four waves, so it owns four
-// waves' worth of consecutive pages.  AKV_PAGES_PER_WAVE overrides (sweeps).
-SplitPlan plan_int8_splits(const akv_dims* d, int batch, int max_pages) {
+// share of the page-heads, at least min_ppw pages so the per-wave set-up, the
+// first page's latency and the end-of-split merge stay small.  Measured at 32K
+// (496 pages x 4 KV heads): the int8 call alone runs best with 2 pages per wave
+// (19.2 us against 20.7 with 3 and 24.4 with 4), the hybrid call with 3.  A
+// work-group is four waves, so it owns four waves' worth of consecutive pages.
+// AKV_PAGES_PER_WAVE overrides (sweeps).
+SplitPlan plan_int8_splits(const akv_dims* d, int batch, int max_pages, int min_ppw) {
     SplitPlan p{1, 0};
     if (batch <= 0 || max_pages <= 0) return p;
     long long units = (long long)batch * d->num_kv_heads * max_pages;
-    int ppw = (int)std::max<long long>(3, (units + 2047) / 2048);
+    int ppw = (int)std::max<long long>(min_ppw, (units + 2047) / 2048);
     if (const char* e = getenv("AKV_PAGES_PER_WAVE")) {
         int v = atoi(e);
         if (v > 0) ppw = v;
@@ -114,7 +116,7 @@ static int env_int(const char* name) {
 
 void plan_hybrid(const akv_dims* d, int batch, int max_pages_int8, int max_pages_window, SplitPlan* p8,
                  SplitPlan* pw) {
-    *p8 = plan_int8_splits(d, batch, max_pages_int8);
+    *p8 = plan_int8_splits(d, batch, max_pages_int8, 3);
     *pw = plan_window_splits(d, batch, max_pages_window);
     if (batch <= 0 || max_pages_window <= 0 || max_pages_int8 <= 0) return;
     const long long units = (long long)batch * d->num_kv_heads;

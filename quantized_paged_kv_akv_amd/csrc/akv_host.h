@@ -38,7 +38,7 @@ SplitPlan plan_splits(const akv_dims* d, int batch, int max_pages);
 // them near-equally over their four waves, each of which stages at most
 // kMaxPagesPerWave page slots.
 constexpr int kMaxPagesPerWave = 64;
-SplitPlan plan_int8_splits(const akv_dims* d, int batch, int max_pages);
+SplitPlan plan_int8_splits(const akv_dims* d, int batch, int max_pages, int min_ppw = 2);
 
 // Workspace bytes for `batch` requests with `n_splits` splits each.
 size_t partial_bytes(const akv_dims* d, int batch, int n_splits);
