@@ -122,6 +122,21 @@ __device__ __forceinline__ void split_f16x2(float x0, float x1, half2& hi, half2
     hi = half2{(_Float16)x0, (_Float16)x1};
     lo = half2{(_Float16)(x0 - (float)hi[0]), (_Float16)(x1 - (float)hi[1])};
 }
+// The hi part fp16(x) in lanes with m = 0, the lo part fp16(x - hi) in lanes
+// with m = 1: x - m * hi is exact either way, so this is the same value as
+// selecting between split_f16x2's outputs, without the select.
+__device__ __forceinline__ half2 split_sel_f16x2(float x0, float x1, float m) {
+#pragma clang fp contract(off)
+    const half2 hi = half2{(_Float16)x0, (_Float16)x1};
+    return half2{(_Float16)__builtin_fmaf(-m, (float)hi[0], x0), (_Float16)__builtin_fmaf(-m, (float)hi[1], x1)};
+}
+// split_sel_f16x2 of x = a*b rounded to FP32 (see split_prod_f16x2).
+__device__ __forceinline__ half2 split_prod_sel_f16x2(float a0, float b0, float a1, float b1, float m) {
+#pragma clang fp contract(off)
+    float x0 = a0 * b0, x1 = a1 * b1;
+    asm volatile("" : "+v"(x0), "+v"(x1));
+    return split_sel_f16x2(x0, x1, m);
+}
 __device__ __forceinline__ void split_f16(float x, _Float16& hi, _Float16& lo) {
 #pragma clang fp contract(off)
     hi = (_Float16)x;

@@ -97,18 +97,21 @@ __device__ __forceinline__ void gather_logits(const float (*part)[16][64], int l
 }
 
 // Online-softmax step on this lane's 16 base-2 logits (masked = -inf):
-// returns alpha (rescale of previous state) and writes P.
+// returns alpha (rescale of previous state) and writes P.  The weights come
+// from the hardware base-2 exponential (v_exp_f32) without the library's
+// denormal range fix-up: a weight below 2^-126 may become 0, far below what
+// the FP32 sums of weights around 1 can resolve.
 __device__ __forceinline__ float softmax_step(const float z[16], float& M, float& lsum, float p[16]) {
     float pm = -INFINITY;
 #pragma unroll
     for (int k = 0; k < 16; ++k) pm = fmaxf(pm, z[k]);
     pm = group_max(pm);
     const float Mn = fmaxf(M, pm);
-    const float alpha = exp2f(M - Mn);
+    const float alpha = __builtin_amdgcn_exp2f(M - Mn);
     float ps = 0.0f;
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-        p[k] = exp2f(z[k] - Mn);
+        p[k] = __builtin_amdgcn_exp2f(z[k] - Mn);
         ps += p[k];
     }
     lsum = lsum * alpha + ps;
@@ -126,11 +129,11 @@ __device__ __forceinline__ float softmax_step_int(const float z[16], float& M, f
     for (int k = 0; k < 16; ++k) pm = fmaxf(pm, z[k]);
     pm = group_max(pm);
     const float Mn = fmaxf(M, ceilf(pm));
-    const float alpha = exp2f(M - Mn);
+    const float alpha = __builtin_amdgcn_exp2f(M - Mn);
     float ps = 0.0f;
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-        p[k] = exp2f(z[k] - Mn);
+        p[k] = __builtin_amdgcn_exp2f(z[k] - Mn);
         ps += p[k];
     }
     lsum = lsum * alpha + ps;
@@ -217,6 +220,7 @@ __device__ __forceinline__ void int8_split(const Int8Args& a, Int8Smem& sm, int 
     // lo part in odd ones (adjacent lanes add them back together)
     const int hh = n >> 1;
     const bool lo_lane = (n & 1) != 0;
+    const float lo_m = lo_lane ? 1.0f : 0.0f;
     // wave w reads the work-group's pages w, w + 4, w + 8, ...: at any moment
     // the four waves stream neighbouring pages, which the memory system serves
     // better than four distant ranges.  The loop runs p = pa .. pb - 1 over
@@ -320,9 +324,7 @@ __device__ __forceinline__ void int8_split(const Int8Args& a, Int8Smem& sm, int 
                     const f32x4 qq = qr[i4], cc = cr[i4];
 #pragma unroll
                     for (int e = 0; e < 4; e += 2) {
-                        half2 hi, lo;
-                        split_prod_f16x2(qq[e], cc[e], qq[e + 1], cc[e + 1], hi, lo);
-                        const half2 v = lo_lane ? lo : hi;
+                        const half2 v = split_prod_sel_f16x2(qq[e], cc[e], qq[e + 1], cc[e + 1], lo_m);
                         const int ix = 4 * i4 + e;
                         qb[ix >> 3][ix & 7] = v[0];
                         qb[ix >> 3][(ix & 7) + 1] = v[1];
@@ -359,9 +361,7 @@ __device__ __forceinline__ void int8_split(const Int8Args& a, Int8Smem& sm, int 
             for (int s = 0; s < 2; ++s)
 #pragma unroll
                 for (int e = 0; e < 8; e += 2) {
-                    half2 hi, lo;
-                    split_f16x2(p_elem(pr, s, e), p_elem(pr, s, e + 1), hi, lo);
-                    const half2 v = lo_lane ? lo : hi;
+                    const half2 v = split_sel_f16x2(p_elem(pr, s, e), p_elem(pr, s, e + 1), lo_m);
                     pbo[s][e] = v[0];
                     pbo[s][e + 1] = v[1];
                 }
