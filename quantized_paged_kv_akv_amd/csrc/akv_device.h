@@ -142,6 +142,12 @@ __device__ __forceinline__ void split_f16(float x, _Float16& hi, _Float16& lo) {
     hi = (_Float16)x;
     lo = (_Float16)(x - (float)hi);
 }
+// BF16 counterpart of split_sel_f16x2: bf16(x) for m = 0, bf16(x - bf16(x)) for m = 1.
+__device__ __forceinline__ __bf16 split_sel_bf16(float x, float m) {
+#pragma clang fp contract(off)
+    const __bf16 hi = (__bf16)x;
+    return (__bf16)__builtin_fmaf(-m, (float)hi, x);
+}
 __device__ __forceinline__ void split_bf16(float x, __bf16& hi, __bf16& lo) {
 #pragma clang fp contract(off)
     hi = (__bf16)x;

@@ -636,6 +636,7 @@ __device__ __forceinline__ void exact_split(const ExactArgs& a, const Src& src, 
 
     typename Src::Page cur;
     src.load(pt[p0], kvh, Hkv, w, l, cur);
+    const float vm = valid ? 1.0f : 0.0f, lo_m = hi_lane ? 0.0f : 1.0f;
 
     float M = -INFINITY, lsum = 0.0f;
     f32x4 O[4];
@@ -660,27 +661,29 @@ __device__ __forceinline__ void exact_split(const ExactArgs& a, const Src& src, 
         __syncthreads();
 
         const int in_page = len - p * kP;  // valid tokens in this page (>= 1)
+        const bool partial = in_page < kP;
         float S[16], z[16], pr[16];
         gather_logits(s_part[it & 1], l, S);
+        if (partial) {
 #pragma unroll
-        for (int k = 0; k < 16; ++k) z[k] = (16 * g + k < in_page) ? S[k] * a.scale_log2 : -INFINITY;
+            for (int k = 0; k < 16; ++k) z[k] = (16 * g + k < in_page) ? S[k] * a.scale_log2 : -INFINITY;
+        } else {
+#pragma unroll
+            for (int k = 0; k < 16; ++k) z[k] = S[k] * a.scale_log2;
+        }
         const float alpha = softmax_step(z, M, lsum, pr);
 
+        // P^T operand: the hi part in hi lanes, the lo part in lo lanes, 0 for heads past G
         bf16x8 pb[2];
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
-            for (int e2 = 0; e2 < 8; ++e2) {
-                __bf16 hi, lo;
-                split_bf16(p_elem(pr, s, e2), hi, lo);
-                pb[s][e2] = valid ? (hi_lane ? hi : lo) : (__bf16)0.0f;
-            }
+            for (int e2 = 0; e2 < 8; ++e2) pb[s][e2] = split_sel_bf16(p_elem(pr, s, e2) * vm, lo_m);
 
 #pragma unroll
         for (int j = 0; j < 4; ++j) O[j] = O[j] * alpha;
         // value register 2j + s is channel tile j, contraction half s (tokens 16g + 8s ..);
         // on the last, partial page masked values must not reach the MFMA
-        const bool partial = in_page < kP;
         src.values(cur, [&](int r, u32x4 vop) {
             if (partial) vop = mask_tokens(vop, 16 * g + 8 * (r & 1), in_page);
             O[r >> 1] = mfma_bf16(as_bf16x8(vop), pb[r & 1], O[r >> 1]);
