@@ -99,59 +99,29 @@ __device__ __forceinline__ float swap_pair(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
 }
 
-// x = a*b rounded to FP32, split as hi + lo with hi = fp16(x) and
-// lo = fp16(x - hi).  Contraction is off: fusing a*b into the conversions
-// would round hi two different ways and break hi + lo ~ x.
-__device__ __forceinline__ void split_prod_f16(float a, float b, _Float16& hi, _Float16& lo) {
-#pragma clang fp contract(off)
-    float x = a * b;
-    asm volatile("" : "+v"(x));  // x is a rounded FP32 value: no mixed-precision fusion through it
-    hi = (_Float16)x;
-    lo = (_Float16)(x - (float)hi);
-}
-// Two at a time with the packed conversions (v_cvt_pk_f16_f32).
-__device__ __forceinline__ void split_prod_f16x2(float a0, float b0, float a1, float b1, half2& hi, half2& lo) {
-#pragma clang fp contract(off)
-    float x0 = a0 * b0, x1 = a1 * b1;
-    asm volatile("" : "+v"(x0), "+v"(x1));
-    hi = half2{(_Float16)x0, (_Float16)x1};
-    lo = half2{(_Float16)(x0 - (float)hi[0]), (_Float16)(x1 - (float)hi[1])};
-}
-__device__ __forceinline__ void split_f16x2(float x0, float x1, half2& hi, half2& lo) {
-#pragma clang fp contract(off)
-    hi = half2{(_Float16)x0, (_Float16)x1};
-    lo = half2{(_Float16)(x0 - (float)hi[0]), (_Float16)(x1 - (float)hi[1])};
-}
-// The hi part fp16(x) in lanes with m = 0, the lo part fp16(x - hi) in lanes
-// with m = 1: x - m * hi is exact either way, so this is the same value as
-// selecting between split_f16x2's outputs, without the select.
+// An FP32 operand x enters a half-precision MFMA as hi + lo with
+// hi = fp16(x) and lo = fp16(x - hi), the two parts in neighbouring columns.
+// A lane takes the hi part when m = 0 and the lo part when m = 1: x - m * hi
+// is exact either way (hi keeps the leading bits of x), so no select is needed.
 __device__ __forceinline__ half2 split_sel_f16x2(float x0, float x1, float m) {
 #pragma clang fp contract(off)
     const half2 hi = half2{(_Float16)x0, (_Float16)x1};
     return half2{(_Float16)__builtin_fmaf(-m, (float)hi[0], x0), (_Float16)__builtin_fmaf(-m, (float)hi[1], x1)};
 }
-// split_sel_f16x2 of x = a*b rounded to FP32 (see split_prod_f16x2).
+// The same for x = a*b rounded to FP32.  Contraction is off and the product
+// is pinned: fusing a*b into the conversions would round hi two different
+// ways and break hi + lo ~ x.
 __device__ __forceinline__ half2 split_prod_sel_f16x2(float a0, float b0, float a1, float b1, float m) {
 #pragma clang fp contract(off)
     float x0 = a0 * b0, x1 = a1 * b1;
-    asm volatile("" : "+v"(x0), "+v"(x1));
+    asm volatile("" : "+v"(x0), "+v"(x1));  // rounded FP32 values: no mixed-precision fusion through them
     return split_sel_f16x2(x0, x1, m);
 }
-__device__ __forceinline__ void split_f16(float x, _Float16& hi, _Float16& lo) {
-#pragma clang fp contract(off)
-    hi = (_Float16)x;
-    lo = (_Float16)(x - (float)hi);
-}
-// BF16 counterpart of split_sel_f16x2: bf16(x) for m = 0, bf16(x - bf16(x)) for m = 1.
+// BF16 parts: bf16(x) for m = 0, bf16(x - bf16(x)) for m = 1.
 __device__ __forceinline__ __bf16 split_sel_bf16(float x, float m) {
 #pragma clang fp contract(off)
     const __bf16 hi = (__bf16)x;
     return (__bf16)__builtin_fmaf(-m, (float)hi, x);
-}
-__device__ __forceinline__ void split_bf16(float x, __bf16& hi, __bf16& lo) {
-#pragma clang fp contract(off)
-    hi = (__bf16)x;
-    lo = (__bf16)(x - (float)hi);
 }
 
 // Exact-tier page order: QK tile t, A-operand row i is token
