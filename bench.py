@@ -655,8 +655,8 @@ def main():
                     help="for counter runs: a 1 GiB device copy (calibration), then --steps hybrid steps; no JSON")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only (the path is measured on one GPU's share; "
-              "sharding across GPUs is described in DESIGN.md, not built). Use --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only (one GPU's share of the path at its real shape; sharding by KV "
+              "head, request or page range needs no new kernel and is not run here). Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     from quantized_paged_kv_akv_amd import configs

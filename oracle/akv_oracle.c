@@ -25,7 +25,7 @@
  *           empty partial.  "ActiveKV" systems page, section "The idea": the
  *           two tiers combine with exact attention arithmetic.
  *
- * Readings where the pages are silent (each also listed in the design doc):
+ * Readings where the pages are silent:
  *   - "RMS over the page" = sqrt(mean over the page's tokens of K^2), per
  *     (page, KV head, channel).  The factor is sqrt(RMS) = ms^(1/4).
  *   - Normalisation divides by the geometric mean of the factors of the
