@@ -275,6 +275,7 @@ __device__ __forceinline__ void int8_split(const Int8Args& a, Int8Smem& sm, int 
     stage_row(r0, qraw0);  // zero rows stay zero: frexp(0) gives e = 0
     stage_row(r1, qraw1);
     __syncthreads();
+    const float qsc = ldexpf(1.0f, (int)sm.qe[hh]);  // undoes the staging scale of this lane's head
 
     float M = -INFINITY, lsum = 0.0f;
     f32x4 O[16];
@@ -344,7 +345,6 @@ __device__ __forceinline__ void int8_split(const Int8Args& a, Int8Smem& sm, int 
 #pragma unroll
                 for (int r = 0; r < 4; ++r) S[t][r] += swap_pair(S[t][r]);
             // logits (base 2): the token factor multiplies the finished dot product
-            const float qsc = exp2f(sm.qe[hh]);
             const f32x4* tk = reinterpret_cast<const f32x4*>(&scl[2 * kD + 16 * g]);
             float z[16], pr[16];
 #pragma unroll
