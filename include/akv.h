@@ -106,6 +106,30 @@ const char *akv_version(void);
 akv_status akv_set_profile_events(void *start_event, void *stop_event);
 
 /*
+ * Instrumentation (launch-shape sweeps and tests): on the calling thread,
+ * override how the decode calls split their pages over work-groups.  Each
+ * field is 0 for the library's own plan, else:
+ *   pages_per_split      akv_decode_attn_exact / _l13: pages per work-group;
+ *   pages_per_wave       akv_decode_attn_int8: pages per wave (a work-group is
+ *                        four waves), at most 64;
+ *   hybrid_int8_pages    akv_decode_hybrid: int8 pages per work-group, at
+ *                        most 256;
+ *   hybrid_window_pages  akv_decode_hybrid: window pages per work-group.
+ * NULL restores the plan.  The workspace size queries follow the same
+ * setting, so change it only between a query and the calls it sized.
+ * Results do not depend on the shape beyond FP32 rounding order.
+ * Errors: AKV_ERR_ARG for a negative field or one beyond its limit (nothing
+ * is changed then).
+ */
+typedef struct {
+    int32_t pages_per_split;
+    int32_t pages_per_wave;
+    int32_t hybrid_int8_pages;
+    int32_t hybrid_window_pages;
+} akv_launch_shape;
+akv_status akv_set_launch_shape(const akv_launch_shape *shape);
+
+/*
  * Instrumentation: one plain streaming read of `bytes` (a multiple of 16 at
  * least 32 KiB) of device memory at `buf` (16-byte aligned) with non-temporal
  * 16-byte vector loads from 2048 work-groups, the streaming-read ceiling the decode
@@ -128,8 +152,12 @@ akv_status akv_stream_read(const void *buf, size_t bytes, uint32_t *sink, void *
  *   value scale         vs_d = max_t |V[t][d]| / 127;
  *   codes               round-half-even(K / (c_d s_t)), round-half-even(V / vs_d),
  *                       clamped to [-127, 127]; a zero scale gives code 0.
- * Scale arithmetic is float64, stored FP32 (round to nearest); the code
- * quotient is an IEEE float64 divide of the FP32 scales' exact product.
+ * Scales are stored FP32 (round to nearest).  The channel factor's sums,
+ * root and geometric mean are float64; the token maximum max_d |K| / c_d is
+ * taken over FP32 products |K| * (1 / c_d), within one FP32 ulp of the
+ * float64 maximum, and then divided by 127 in float64; the value scale's
+ * maximum is exact.  Each code is exactly round-half-even of the float64
+ * quotient x / (c_d s_t) (x / vs_d) for the FP32 scales the call stores.
  * Only full pages are accepted: a page still being written is served by the
  * exact tier until it is converted.
  *
@@ -243,10 +271,10 @@ akv_status akv_merge_lse(int32_t rows, int32_t head_dim, float *acc_o, float *ac
 akv_status akv_fill_empty(int32_t rows, int32_t head_dim, float *o, float *lse, void *stream);
 
 /*
- * Streaming page publication ("ActiveKV" page, "What I built"): a page leaves
- * the exact window only once it is full in every layer; its conversion runs
- * beside decode and never stalls it, and until it is published decode keeps
- * serving it exact.
+ * Streaming page publication ("Model quantization" page, "An 8-bit page
+ * format shaped for its kernel": pages are converted in the background, and
+ * only once they are full in every layer; a page not yet published is read
+ * by the exact tier, so decode never waits for a conversion).
  *
  * akv_publish_pages: on side_stream, waits for ready_event (if not NULL;
  *   recorded by the caller on its compute stream once the pages are full),

@@ -36,6 +36,11 @@ class akv_dims(ctypes.Structure):
     _fields_ = [("num_kv_heads", _i32), ("group", _i32), ("head_dim", _i32), ("page_size", _i32)]
 
 
+class akv_launch_shape(ctypes.Structure):
+    _fields_ = [("pages_per_split", _i32), ("pages_per_wave", _i32), ("hybrid_int8_pages", _i32),
+                ("hybrid_window_pages", _i32)]
+
+
 def dims(num_kv_heads: int, group: int, head_dim: int = 256, page_size: int = 64) -> akv_dims:
     return akv_dims(num_kv_heads, group, head_dim, page_size)
 
@@ -47,6 +52,7 @@ _SIGS = {
     "akv_last_error": (ctypes.c_char_p, []),
     "akv_version": (ctypes.c_char_p, []),
     "akv_set_profile_events": (ctypes.c_int, [_vp, _vp]),
+    "akv_set_launch_shape": (ctypes.c_int, [ctypes.c_void_p]),
     "akv_quantize_pages": (ctypes.c_int, [_D, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "akv_decode_workspace_bytes": (_sz, [_D, _i32, _i32]),
     "akv_decode_attn_int8": (ctypes.c_int, [_D, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _f32,
@@ -130,6 +136,17 @@ def akv_set_profile_events(start_event=None, stop_event=None):
     a = _vp(start_event.cuda_event) if start_event is not None else _vp(0)
     b = _vp(stop_event.cuda_event) if stop_event is not None else _vp(0)
     _check("akv_set_profile_events", _lib.akv_set_profile_events(a, b))
+
+
+def akv_set_launch_shape(pages_per_split: int = 0, pages_per_wave: int = 0, hybrid_int8_pages: int = 0,
+                         hybrid_window_pages: int = 0, reset: bool = False):
+    """Launch-shape override of the calling thread (0 = planned); reset=True
+    (or all zero) restores the library's plan."""
+    if reset:
+        _check("akv_set_launch_shape", _lib.akv_set_launch_shape(None))
+        return
+    s = akv_launch_shape(pages_per_split, pages_per_wave, hybrid_int8_pages, hybrid_window_pages)
+    _check("akv_set_launch_shape", _lib.akv_set_launch_shape(ctypes.byref(s)))
 
 
 def akv_quantize_pages(d: akv_dims, n: int, k_bf16, v_bf16, src_slot, dst_slot, k_codes, v_codes, k_chan,

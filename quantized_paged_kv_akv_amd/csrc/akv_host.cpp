@@ -23,6 +23,8 @@ void clear_error() { g_err[0] = '\0'; }
 
 static thread_local hipEvent_t g_prof_start = nullptr;
 static thread_local hipEvent_t g_prof_stop = nullptr;
+// launch-shape overrides of the calling thread (akv_set_launch_shape); 0 = planned
+static thread_local akv_launch_shape g_shape = {0, 0, 0, 0};
 
 hipEvent_t prof_start_event() { return g_prof_start; }
 hipEvent_t prof_stop_event() { return g_prof_stop; }
@@ -40,18 +42,15 @@ akv_status check_dims(const akv_dims* d) {
 
 // Enough work-groups to cover the 256 compute units several times over, but
 // at least 4 pages per work-group so the split partials (6 KB written per
-// split) stay a few percent of the pages read.  AKV_PAGES_PER_SPLIT overrides
-// the choice (for launch-shape sweeps).
+// split) stay a few percent of the pages read.  The thread's launch shape
+// (akv_set_launch_shape) overrides the choice.
 SplitPlan plan_splits(const akv_dims* d, int batch, int max_pages) {
     SplitPlan p{1, 0};
     if (batch <= 0 || max_pages <= 0) return p;
     long long units = (long long)batch * d->num_kv_heads * max_pages;
     long long target_wgs = 1024;
     int pps = (int)std::max<long long>(4, (units + target_wgs - 1) / target_wgs);
-    if (const char* e = getenv("AKV_PAGES_PER_SPLIT")) {
-        int v = atoi(e);
-        if (v > 0) pps = v;
-    }
+    if (g_shape.pages_per_split > 0) pps = g_shape.pages_per_split;
     pps = std::min(pps, max_pages);
     p.pages_per_split = pps;
     p.n_splits = (max_pages + pps - 1) / pps;
@@ -64,16 +63,13 @@ SplitPlan plan_splits(const akv_dims* d, int batch, int max_pages) {
 // (496 pages x 4 KV heads): the int8 call alone runs best with 2 pages per wave
 // (19.2 us against 20.7 with 3 and 24.4 with 4), the hybrid call with 3.  A
 // work-group is four waves, so it owns four waves' worth of consecutive pages.
-// AKV_PAGES_PER_WAVE overrides (sweeps).
+// The thread's launch shape overrides the choice.
 SplitPlan plan_int8_splits(const akv_dims* d, int batch, int max_pages, int min_ppw) {
     SplitPlan p{1, 0};
     if (batch <= 0 || max_pages <= 0) return p;
     long long units = (long long)batch * d->num_kv_heads * max_pages;
     int ppw = (int)std::max<long long>(min_ppw, (units + 2047) / 2048);
-    if (const char* e = getenv("AKV_PAGES_PER_WAVE")) {
-        int v = atoi(e);
-        if (v > 0) ppw = v;
-    }
+    if (g_shape.pages_per_wave > 0) ppw = g_shape.pages_per_wave;
     ppw = std::min(ppw, kMaxPagesPerWave);
     p.pages_per_split = std::min(4 * ppw, max_pages);
     p.n_splits = (max_pages + p.pages_per_split - 1) / p.pages_per_split;
@@ -109,11 +105,6 @@ int device_cu_count() {
     return cached_cus;
 }
 
-static int env_int(const char* name) {
-    const char* e = getenv(name);
-    return e ? atoi(e) : 0;
-}
-
 void plan_hybrid(const akv_dims* d, int batch, int max_pages_int8, int max_pages_window, SplitPlan* p8,
                  SplitPlan* pw) {
     *p8 = plan_int8_splits(d, batch, max_pages_int8, 3);
@@ -137,11 +128,11 @@ void plan_hybrid(const akv_dims* d, int batch, int max_pages_int8, int max_pages
         // stay free, which streams slightly better than a completely full chip
         if ((q8 + 3) / 4 <= kMaxPagesPerWave) *p8 = SplitPlan{q8, (max_pages_int8 + q8 - 1) / q8};
     }
-    if (int v = env_int("AKV_HYBRID_INT8_PAGES")) {
-        const int q8 = std::min(std::min(v, 4 * kMaxPagesPerWave), max_pages_int8);
+    if (g_shape.hybrid_int8_pages > 0) {
+        const int q8 = std::min(std::min(g_shape.hybrid_int8_pages, 4 * kMaxPagesPerWave), max_pages_int8);
         *p8 = SplitPlan{q8, (max_pages_int8 + q8 - 1) / q8};
     }
-    if (int v = env_int("AKV_HYBRID_WINDOW_PAGES")) qw = v;
+    if (g_shape.hybrid_window_pages > 0) qw = g_shape.hybrid_window_pages;
     qw = std::min(qw, max_pages_window);
     *pw = SplitPlan{qw, (max_pages_window + qw - 1) / qw};
 }
@@ -179,6 +170,22 @@ extern "C" akv_status akv_set_profile_events(void* start_event, void* stop_event
         return akv::fail(AKV_ERR_ARG, "set both profile events or neither");
     akv::g_prof_start = (hipEvent_t)start_event;
     akv::g_prof_stop = (hipEvent_t)stop_event;
+    return AKV_OK;
+}
+
+extern "C" akv_status akv_set_launch_shape(const akv_launch_shape* shape) {
+    akv::clear_error();
+    if (!shape) {
+        akv::g_shape = akv_launch_shape{0, 0, 0, 0};
+        return AKV_OK;
+    }
+    if (shape->pages_per_split < 0 || shape->pages_per_wave < 0 || shape->hybrid_int8_pages < 0 ||
+        shape->hybrid_window_pages < 0)
+        return akv::fail(AKV_ERR_ARG, "launch shape fields must be >= 0 (0 = planned)");
+    if (shape->pages_per_wave > akv::kMaxPagesPerWave || shape->hybrid_int8_pages > 4 * akv::kMaxPagesPerWave)
+        return akv::fail(AKV_ERR_ARG, "launch shape beyond %d pages per wave (%d per int8 work-group)",
+                         akv::kMaxPagesPerWave, 4 * akv::kMaxPagesPerWave);
+    akv::g_shape = *shape;
     return AKV_OK;
 }
 

@@ -50,8 +50,8 @@ SplitPlan plan_window_splits(const akv_dims* d, int batch, int max_pages);
 // Both tiers of akv_decode_hybrid: window work-groups stream about as many
 // bytes as int8 ones, and when the grid would spill just past one round of
 // resident work-groups (two per compute unit) the int8 work-groups widen so
-// that it fits.  AKV_HYBRID_INT8_PAGES / AKV_HYBRID_WINDOW_PAGES override the
-// pages per work-group of each tier (launch-shape sweeps).
+// that it fits.  The thread's launch shape (akv_set_launch_shape) overrides
+// the pages per work-group of each tier.
 void plan_hybrid(const akv_dims* d, int batch, int max_pages_int8, int max_pages_window, SplitPlan* p8,
                  SplitPlan* pw);
 

@@ -906,14 +906,27 @@ extern "C" akv_status akv_decode_hybrid(const akv_dims* dims, int32_t batch, con
     if (st != AKV_OK) return st;
     if (max_pages_window < 0) return fail(AKV_ERR_ARG, "negative max_pages_window");
     if (batch == 0) return AKV_OK;
-    const void* ptrs[] = {q, k_codes, v_codes, k_chan, k_tok, v_chan, k_bf16, v_bf16, out_o, out_lse};
-    const void* tabs[] = {page_table_int8, n_pages_int8, page_table_window, window_len};
-    if ((st = check_ptrs(ptrs, 10, tabs, 4)) != AKV_OK) return st;
+    // a tier with no page-table columns is never read: its pointers may be NULL
+    const void* ptrs_q[] = {q, out_o, out_lse};
+    if ((st = check_ptrs(ptrs_q, 3, nullptr, 0)) != AKV_OK) return st;
+    if (max_pages_int8 > 0) {
+        const void* ptrs[] = {k_codes, v_codes, k_chan, k_tok, v_chan};
+        const void* tabs[] = {page_table_int8, n_pages_int8};
+        if ((st = check_ptrs(ptrs, 5, tabs, 2)) != AKV_OK) return st;
+    }
+    if (max_pages_window > 0) {
+        const void* ptrs[] = {k_bf16, v_bf16};
+        const void* tabs[] = {page_table_window, window_len};
+        if ((st = check_ptrs(ptrs, 2, tabs, 2)) != AKV_OK) return st;
+    }
     const int rows = batch * dims->num_kv_heads * dims->group;
     if (max_pages_int8 + max_pages_window == 0) return akv_fill_empty(rows, dims->head_dim, out_o, out_lse, stream);
     SplitPlan p8, pw;
     plan_hybrid(dims, batch, max_pages_int8, max_pages_window, &p8, &pw);
     if (max_pages_int8 > 0 && (st = check_int8_plan(p8, max_pages_int8)) != AKV_OK) return st;
+    if (pw.n_splits < 0 || (max_pages_window > 0 && pw.n_splits < 1) || (max_pages_int8 == 0 && p8.n_splits != 0))
+        return fail(AKV_ERR_ARG, "hybrid split plan of %d int8 and %d window splits is inconsistent", p8.n_splits,
+                    pw.n_splits);
     const int n_cols = p8.n_splits + pw.n_splits;
     if ((st = check_workspace(workspace, workspace_bytes, partial_bytes(dims, batch, n_cols))) != AKV_OK) return st;
     hipStream_t s = (hipStream_t)stream;

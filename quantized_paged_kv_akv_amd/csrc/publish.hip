@@ -1,7 +1,7 @@
-// publish.hip -- streaming page publication ("ActiveKV" page, "What I built":
-// a page leaves the exact window only once it is full in every layer, its
-// conversion runs beside decode and never stalls it, and until it is
-// published the page is served exact).
+// publish.hip -- streaming page publication ("Model quantization" page, "An
+// 8-bit page format shaped for its kernel": conversion happens in the
+// background and only for pages complete in every layer; an unpublished page
+// stays with the exact tier, so decode never waits for a conversion).
 //
 // akv_publish_pages converts full BF16 pages on a side stream once that
 // stream has seen the caller's "pages complete" event, and records a "done"

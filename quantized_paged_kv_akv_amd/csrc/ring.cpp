@@ -1,9 +1,10 @@
 // ring.cpp -- host-staged mode: layer-at-a-time staging of pinned host history
 // into a ring of caller-owned device slots ("ActiveKV" page, "The idea" and
-// "What I built": history is authoritative in pinned host memory, the device
-// holds a budgeted working set, staging is asynchronous and fence-safe so a
-// buffer is never reused while a copy or kernel still touches it, and an
-// oversized request is refused rather than stalled).
+// "What I built").  The pinned host copy is the authoritative history and the
+// device holds only a budgeted working set; copies are asynchronous, and
+// events order every reuse of a slot after both the copy into it and the
+// kernels reading it have finished; a request too large for a slot is
+// refused up front instead of stalling.
 //
 // Lifecycle of slot s = layer % n_slots:
 //   free --stage--> staged --release--> free

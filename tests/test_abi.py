@@ -117,3 +117,50 @@ def test_lossless_host_side_validation(B):
     assert st == -4
     sz = B.l13_sizes(d, 7)
     assert sz["desc"] == (7, 2, 2) and sz["table"] == (7, 2, 2, 32) and sz["arena_bytes"] == 7 * 2 * 2 * 32768
+
+
+def test_launch_shape_validation(B):
+    """The launch-shape override refuses negative fields and shapes beyond
+    what a wave can stage, leaves the setting unchanged then, and the
+    workspace queries follow the setting that is in force."""
+    lib = B._lib
+    d = B.dims(4, 6)
+    planned = B.akv_decode_workspace_bytes(d, 1, 2032)
+    for bad in (dict(pages_per_split=-1), dict(pages_per_wave=65), dict(hybrid_int8_pages=257),
+                dict(hybrid_window_pages=-3)):
+        with pytest.raises(B.AkvError) as e:
+            B.akv_set_launch_shape(**bad)
+        assert e.value.status_name == "AKV_ERR_ARG"
+        assert B.akv_decode_workspace_bytes(d, 1, 2032) == planned
+    try:
+        B.akv_set_launch_shape(pages_per_split=1, pages_per_wave=1)
+        # one page per exact split: 2032 partial columns per row
+        assert B.akv_decode_workspace_bytes(d, 1, 2032) >= 24 * 2032 * 257 * 4
+        B.akv_set_launch_shape(hybrid_int8_pages=8, hybrid_window_pages=1)
+        need = B.akv_decode_hybrid_workspace_bytes(d, 1, 2032, 16)
+        assert need >= 24 * (254 + 16) * 257 * 4
+    finally:
+        B.akv_set_launch_shape(reset=True)
+    assert B.akv_decode_workspace_bytes(d, 1, 2032) == planned
+    assert lib.akv_set_launch_shape(None) == 0
+
+
+def test_hybrid_empty_tier_pointers_may_be_null(B):
+    """A tier with no page-table columns is never read, so its pointers may be
+    NULL; the other tier's pointers are still checked."""
+    lib = B._lib
+    d = B.dims(4, 6)
+    p, t4, z = ctypes.c_void_p(16), ctypes.c_void_p(20), ctypes.c_void_p(0)
+    # window-only call (max_pages_int8 = 0) with NULL int8 pointers: passes the
+    # pointer checks and stops at the workspace check (16 bytes is too small)
+    st = lib.akv_decode_hybrid(ctypes.byref(d), 1, p, z, z, z, z, z, z, z, 0, p, p, t4, t4, 16, 0.0625, p, p, p,
+                               16, None)
+    assert st == -4, lib.akv_last_error()
+    # int8-only call with NULL window pointers
+    st = lib.akv_decode_hybrid(ctypes.byref(d), 1, p, p, p, p, p, p, t4, t4, 2032, z, z, z, z, 0, 0.0625, p, p, p,
+                               16, None)
+    assert st == -4, lib.akv_last_error()
+    # a NULL pointer of a non-empty tier is refused
+    st = lib.akv_decode_hybrid(ctypes.byref(d), 1, p, p, p, p, p, p, t4, t4, 2032, z, p, t4, t4, 16, 0.0625, p, p,
+                               p, 16, None)
+    assert st == -1

@@ -161,16 +161,18 @@ def test_int8_decode_parity(B, Hkv, G, n_pages):
     check_attn(o, lse, ro, rl, f"int8 Hkv{Hkv} G{G}")
 
 
-@pytest.mark.parametrize("pages_per_wave", [None, "64"])
-def test_int8_long_context(B, monkeypatch, pages_per_wave):
+@pytest.mark.parametrize("pages_per_wave", [0, 64])
+def test_int8_long_context(B, pages_per_wave):
     """A 512K-token history (8192 int8 pages) of one KV head: with the default
     plan, 512 splits (the looping second pass); with 64 pages per wave (the
     launch-shape override), every wave at the 64 page slots it can stage."""
-    if pages_per_wave:
-        monkeypatch.setenv("AKV_PAGES_PER_WAVE", pages_per_wave)
     say(f"case int8 long context 8192 pages, pages per wave {pages_per_wave or 'planned'}")
     g, table, q = _int8_case(B, 808, 1, 4, [8192])
-    o, lse = run_int8(B, 1, 4, q, g, table, [8192])
+    B.akv_set_launch_shape(pages_per_wave=pages_per_wave)
+    try:
+        o, lse = run_int8(B, 1, 4, q, g, table, [8192])
+    finally:
+        B.akv_set_launch_shape(reset=True)
     ro, rl = oracle_int8(O, 1, 4, q, g, table, [8192])
     check_attn(o, lse, ro, rl, "int8 8192 pages")
 
@@ -225,19 +227,22 @@ def test_exact_decode_parity(B, Hkv, G, seq_len):
 
 
 @pytest.mark.parametrize("n_pages", [100, 200, 300])
-def test_split_combine_paths(B, monkeypatch, n_pages):
+def test_split_combine_paths(B, n_pages):
     """One page per split (a launch-shape override) so the split-K second pass
     folds 100, 200 and 300 partials per row: its register paths (up to 128
     and 256 splits) and its looping path; the last page is partial and one
     request is empty."""
-    monkeypatch.setenv("AKV_PAGES_PER_SPLIT", "1")
     seq_len = [64 * n_pages - 17, 0]
     say(f"case split combine n_pages={n_pages}")
     kp, vp = inputs.random_pools(500 + n_pages, n_pages, 1)
     table = np.zeros((2, n_pages), np.int32)
     table[0] = np.random.default_rng(n_pages).permutation(n_pages)
     q = inputs.random_queries(501, 2, 4)
-    o, lse = run_exact(B, 1, 4, q, dev(kp), dev(vp), table, seq_len)
+    B.akv_set_launch_shape(pages_per_split=1)
+    try:
+        o, lse = run_exact(B, 1, 4, q, dev(kp), dev(vp), table, seq_len)
+    finally:
+        B.akv_set_launch_shape(reset=True)
     ro, rl = O.decode_exact(q, kp, vp, table, np.asarray(seq_len, np.int32), 1, 4, SIG)
     check_attn(o, lse, ro, rl, f"combine {n_pages} splits")
 
