@@ -146,3 +146,14 @@ def oracle_int8(O, Hkv, G, q, g, table, n_pages, sigma=1 / 16):
     return O.decode_int8(q, k_codes_token_major(host(g["k_codes"])), host(g["v_codes"]), host(g["k_chan"]), host(g["k_tok"]),
                          host(g["v_chan"]), np.asarray(table, np.int32), np.asarray(n_pages, np.int32), Hkv, G,
                          sigma, mode=0)
+
+
+def oracle_hybrid(O, Hkv, G, q, g, t8, n8, kpool, vpool, tw, win, sigma=1 / 16):
+    """Oracle of one hybrid layer on the GPU's int8 codes: the int8 tier
+    (dequantized pages, dense softmax), the exact window, and their LSE
+    merge.  Returns (O [rows][D], LSE [rows]) with rows = batch * Hkv * G."""
+    rows = int(len(n8)) * Hkv * G
+    ro8, rl8 = oracle_int8(O, Hkv, G, q, g, t8, n8, sigma)
+    row, rlw = O.decode_exact(q, kpool, vpool, np.asarray(tw, np.int32), np.asarray(win, np.int32), Hkv, G, sigma)
+    return O.merge(np.stack([ro8.reshape(rows, 256), row.reshape(rows, 256)]),
+                   np.stack([rl8.reshape(rows), rlw.reshape(rows)]))

@@ -12,8 +12,8 @@ import torch
 
 from oracle import oracle as O
 from quantized_paged_kv_akv_amd import configs, inputs
-from tests.gpu_util import (check_attn, check_quantize, dev, gpu_quantize, host, oracle_int8, run_exact,
-                            run_int8, say, workspace)
+from tests.gpu_util import (check_attn, check_quantize, dev, gpu_quantize, host, oracle_hybrid, oracle_int8,
+                            run_exact, run_int8, say, workspace)
 
 pytestmark = pytest.mark.gpu
 SIG = 1.0 / 16.0
@@ -417,3 +417,68 @@ def test_hybrid_step_replays_from_a_graph(B):
             assert torch.equal(o, ro) and torch.equal(l, rl), f"replay {rep} differs"
         step()  # eager work between replays
         torch.cuda.synchronize()
+
+
+# ----------------------------------------------------------------------------- fused call edge cases
+def _hybrid_custom(B, seed, Hkv, G, n8, win, null_empty_tier=False):
+    """akv_decode_hybrid on hand-made tier splits (n8[b] int8 pages and
+    win[b] window tokens per request, pools permuted) against the oracle on
+    the GPU's codes.  With null_empty_tier, a tier with no pages in any
+    request gets zero page-table columns and NULL pointers."""
+    batch = len(n8)
+    n8_tot, wp = int(sum(n8)), [(t + 63) // 64 for t in win]
+    wp_tot = int(sum(wp))
+    kp8, vp8 = inputs.random_pools(seed, max(1, n8_tot), Hkv)
+    src = np.arange(max(1, n8_tot), dtype=np.int32)
+    dst = np.random.default_rng(seed + 1).permutation(max(1, n8_tot)).astype(np.int32)
+    g = gpu_quantize(B, kp8, vp8, src, dst, max(1, n8_tot), Hkv)
+    kpw, vpw = inputs.random_pools(seed + 2, max(1, wp_tot), Hkv)
+    wslots = np.random.default_rng(seed + 3).permutation(max(1, wp_tot)).astype(np.int32)
+    m8 = 0 if (null_empty_tier and n8_tot == 0) else max(1, max(n8))
+    mw = 0 if (null_empty_tier and wp_tot == 0) else max(1, max(wp))
+    t8 = np.zeros((batch, max(1, m8)), np.int32)
+    tw = np.zeros((batch, max(1, mw)), np.int32)
+    o8 = ow = 0
+    for b in range(batch):
+        t8[b, :n8[b]] = dst[o8:o8 + n8[b]]
+        tw[b, :wp[b]] = wslots[ow:ow + wp[b]]
+        o8 += n8[b]
+        ow += wp[b]
+    q = inputs.random_queries(seed + 4, batch, Hkv * G)
+    d8 = B.dims(Hkv, G)
+    ws = torch.empty(max(16, B.akv_decode_hybrid_workspace_bytes(d8, batch, m8, mw)), dtype=torch.uint8,
+                     device="cuda")
+    ho = torch.full((batch, Hkv * G, 256), float("nan"), device="cuda")
+    hl = torch.full((batch, Hkv * G), float("nan"), device="cuda")
+    i8 = (g["k_codes"], g["v_codes"], g["k_chan"], g["k_tok"], g["v_chan"], dev(t8),
+          dev(np.asarray(n8, np.int32)))
+    wt = (dev(kpw), dev(vpw), dev(tw), dev(np.asarray(win, np.int32)))
+    if m8 == 0:
+        i8 = (None,) * 7
+    if mw == 0:
+        wt = (None,) * 4
+    B.akv_decode_hybrid(d8, batch, dev(q), *i8[:7], m8, *wt, mw, SIG, ho, hl, ws)
+    torch.cuda.synchronize()
+    rm, rl = oracle_hybrid(O, Hkv, G, q, g, t8, n8, kpw, vpw, tw, win)
+    rows = batch * Hkv * G
+    check_attn(ho.view(rows, 256), hl.view(rows), rm, rl, f"hybrid n8={n8} win={win}")
+
+
+@pytest.mark.parametrize("n8,win", [
+    ([0], [300]),                          # context shorter than the window: no int8 page
+    ([0, 61, 0, 1], [300, 1096, 0, 1024]),  # mixed batch with an empty request
+    ([40, 3], [0, 0]),                     # empty windows (window tier launched, every split empty)
+    ([0, 0], [0, 0]),                      # every request empty
+    ([5, 0, 70], [64, 1, 0]),
+])
+def test_hybrid_edge_cases(B, n8, win):
+    say(f"case hybrid edge n8={n8} win={win}")
+    _hybrid_custom(B, 1700 + sum(n8) + sum(win), 4, 6, n8, win)
+
+
+@pytest.mark.parametrize("n8,win", [([0, 0], [700, 65]), ([33, 12], [0, 0])])
+def test_hybrid_one_tier_null_pointers(B, n8, win):
+    """A tier with no page-table columns at all (max_pages = 0) and NULL
+    pointers: the other tier alone, still through the fused call."""
+    say(f"case hybrid single tier n8={n8} win={win}")
+    _hybrid_custom(B, 1800 + sum(n8) + sum(win), 2, 6, n8, win, null_empty_tier=True)
