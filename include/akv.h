@@ -254,6 +254,39 @@ akv_status akv_decode_hybrid(const akv_dims *dims, int32_t batch, const uint16_t
                              void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * akv_decode_hybrid_static -- akv_decode_hybrid without a workspace argument,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  It calls no
+ * allocating routine.  The split partials live in a library-owned device
+ * array of AKV_STATIC_SCRATCH_BYTES on each GPU the library runs on (held
+ * until the process ends); its address is looked up once per device, on the
+ * first call made with that device current.  Same arguments, kernels and
+ * results as akv_decode_hybrid.
+ *
+ * Every call on one GPU shares that GPU's array and leaves its partials
+ * there: two calls that overlap on one GPU (different streams, or threads
+ * without ordering between their streams) race and give wrong results.
+ * Nothing in the array has to start at zero; each call writes every partial
+ * slot it reads.
+ * Errors: as akv_decode_hybrid; AKV_ERR_WORKSPACE (nothing enqueued) when
+ * akv_decode_hybrid_workspace_bytes(dims, batch, max_pages_int8,
+ * max_pages_window) exceeds AKV_STATIC_SCRATCH_BYTES (16 MiB; with the
+ * library's plan at Hkv = 4, G = 6 that holds, e.g., 256 requests of 16K
+ * tokens or one request of 1M tokens);
+ * AKV_ERR_HIP if the array's address cannot be found.
+ */
+#define AKV_STATIC_SCRATCH_BYTES ((size_t)16 << 20)
+akv_status akv_decode_hybrid_static(const akv_dims *dims, int32_t batch, const uint16_t *q,
+                                    const int8_t *k_codes, const int8_t *v_codes,
+                                    const float *k_chan, const float *k_tok, const float *v_chan,
+                                    const int32_t *page_table_int8, const int32_t *n_pages_int8,
+                                    int32_t max_pages_int8,
+                                    const uint16_t *k_bf16, const uint16_t *v_bf16,
+                                    const int32_t *page_table_window, const int32_t *window_len,
+                                    int32_t max_pages_window, float softmax_scale,
+                                    float *out_o, float *out_lse, void *stream);
+
+/*
  * akv_merge_lse -- fold one partial into an FP32 accumulator, exactly.
  * ("SYCL" page, "A merge that joins the tiers".)
  *

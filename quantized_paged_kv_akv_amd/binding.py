@@ -62,6 +62,8 @@ _SIGS = {
     "akv_decode_hybrid_workspace_bytes": (_sz, [_D, _i32, _i32, _i32]),
     "akv_decode_hybrid": (ctypes.c_int, [_D, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp,
                                          _vp, _i32, _f32, _vp, _vp, _vp, _sz, _vp]),
+    "akv_decode_hybrid_static": (ctypes.c_int, [_D, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp,
+                                                _vp, _vp, _i32, _f32, _vp, _vp, _vp]),
     "akv_merge_lse": (ctypes.c_int, [_i32, _i32, _vp, _vp, _vp, _vp, _vp]),
     "akv_fill_empty": (ctypes.c_int, [_i32, _i32, _vp, _vp, _vp]),
     "akv_stream_read": (ctypes.c_int, [_vp, _sz, _vp, _vp]),
@@ -205,6 +207,25 @@ def akv_decode_hybrid(d: akv_dims, batch: int, q, k_codes, v_codes, k_chan, k_to
         max_pages_window, softmax_scale, _ptr(out_o, torch.float32, "out_o"),
         _ptr(out_lse, torch.float32, "out_lse"),
         _ptr(workspace, (torch.uint8, torch.int8, torch.float32), "workspace"), ws_bytes, _stream(stream)))
+
+
+STATIC_SCRATCH_BYTES = 16 << 20  # AKV_STATIC_SCRATCH_BYTES
+
+
+def akv_decode_hybrid_static(d: akv_dims, batch: int, q, k_codes, v_codes, k_chan, k_tok, v_chan,
+                             page_table_int8, n_pages_int8, max_pages_int8: int, k_bf16, v_bf16, page_table_window,
+                             window_len, max_pages_window: int, softmax_scale: float, out_o, out_lse, stream=None):
+    """akv_decode_hybrid with its split partials in the library's static
+    per-device scratch array (no workspace argument, nothing allocated)."""
+    _check("akv_decode_hybrid_static", _lib.akv_decode_hybrid_static(
+        ctypes.byref(d), batch, _ptr(q, _BF16, "q"), _ptr(k_codes, torch.int8, "k_codes"),
+        _ptr(v_codes, torch.int8, "v_codes"), _ptr(k_chan, torch.float32, "k_chan"),
+        _ptr(k_tok, torch.float32, "k_tok"), _ptr(v_chan, torch.float32, "v_chan"),
+        _ptr(page_table_int8, torch.int32, "page_table_int8"), _ptr(n_pages_int8, torch.int32, "n_pages_int8"),
+        max_pages_int8, _ptr(k_bf16, _BF16, "k_bf16"), _ptr(v_bf16, _BF16, "v_bf16"),
+        _ptr(page_table_window, torch.int32, "page_table_window"), _ptr(window_len, torch.int32, "window_len"),
+        max_pages_window, softmax_scale, _ptr(out_o, torch.float32, "out_o"),
+        _ptr(out_lse, torch.float32, "out_lse"), _stream(stream)))
 
 
 def akv_merge_lse(rows: int, head_dim: int, acc_o, acc_lse, part_o, part_lse, stream=None):

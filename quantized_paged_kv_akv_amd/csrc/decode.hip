@@ -39,6 +39,7 @@
 // workspace; combine_kernel folds them exactly.
 #include <math.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "akv_device.h"
@@ -825,6 +826,33 @@ static ExactArgs exact_args(const akv_dims* dims, const uint16_t* q, const uint1
     return a;
 }
 
+// Split partials of akv_decode_hybrid_static: a file-scope device array, one
+// copy per GPU, held until the process ends.  In host code `scratch` is only
+// a stand-in for the symbol; its device address (different on every GPU) is
+// looked up once per device with that device current and used from then on.
+constexpr size_t kStaticScratchBytes = AKV_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+static akv_status static_scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return fail(AKV_ERR_HIP, "no current HIP device (or device id %d beyond %d)", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(AKV_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return AKV_OK;
+}
+
 // Launch the split-K kernel; with profile events set, through
 // hipExtLaunchKernelGGL so the events time the kernel itself.
 template <typename... A>
@@ -893,15 +921,18 @@ extern "C" akv_status akv_decode_attn_exact(const akv_dims* dims, int32_t batch,
     return launch_combine(rows, dims->head_dim, a.part_o, a.part_lse, plan.n_splits, out_o, out_lse, s);
 }
 
-extern "C" akv_status akv_decode_hybrid(const akv_dims* dims, int32_t batch, const uint16_t* q,
-                                        const int8_t* k_codes, const int8_t* v_codes, const float* k_chan,
-                                        const float* k_tok, const float* v_chan, const int32_t* page_table_int8,
-                                        const int32_t* n_pages_int8, int32_t max_pages_int8, const uint16_t* k_bf16,
-                                        const uint16_t* v_bf16, const int32_t* page_table_window,
-                                        const int32_t* window_len, int32_t max_pages_window, float softmax_scale,
-                                        float* out_o, float* out_lse, void* workspace, size_t workspace_bytes,
-                                        void* stream) {
-    clear_error();
+// One hybrid layer with its split partials in `workspace`.  With
+// static_scratch set, the workspace is the library's per-device scratch
+// array: its address is looked up (once per device) only after every host
+// check has passed, and a plan that needs more than the array is refused.
+static akv_status decode_hybrid_impl(const akv_dims* dims, int32_t batch, const uint16_t* q, const int8_t* k_codes,
+                                     const int8_t* v_codes, const float* k_chan, const float* k_tok,
+                                     const float* v_chan, const int32_t* page_table_int8,
+                                     const int32_t* n_pages_int8, int32_t max_pages_int8, const uint16_t* k_bf16,
+                                     const uint16_t* v_bf16, const int32_t* page_table_window,
+                                     const int32_t* window_len, int32_t max_pages_window, float softmax_scale,
+                                     float* out_o, float* out_lse, void* workspace, size_t workspace_bytes,
+                                     bool static_scratch, void* stream) {
     akv_status st = check_shape(dims, batch, max_pages_int8);
     if (st != AKV_OK) return st;
     if (max_pages_window < 0) return fail(AKV_ERR_ARG, "negative max_pages_window");
@@ -928,6 +959,14 @@ extern "C" akv_status akv_decode_hybrid(const akv_dims* dims, int32_t batch, con
         return fail(AKV_ERR_ARG, "hybrid split plan of %d int8 and %d window splits is inconsistent", p8.n_splits,
                     pw.n_splits);
     const int n_cols = p8.n_splits + pw.n_splits;
+    if (static_scratch) {
+        const size_t need = partial_bytes(dims, batch, n_cols);
+        if (need > kStaticScratchBytes)
+            return fail(AKV_ERR_WORKSPACE, "split partials need %zu bytes, the static scratch holds %zu", need,
+                        kStaticScratchBytes);
+        if ((st = static_scratch_address(&workspace)) != AKV_OK) return st;
+        workspace_bytes = kStaticScratchBytes;
+    }
     if ((st = check_workspace(workspace, workspace_bytes, partial_bytes(dims, batch, n_cols))) != AKV_OK) return st;
     hipStream_t s = (hipStream_t)stream;
     Int8Args a8 = int8_args(dims, q, k_codes, v_codes, k_chan, k_tok, v_chan, page_table_int8, n_pages_int8,
@@ -943,6 +982,35 @@ extern "C" akv_status akv_decode_hybrid(const akv_dims* dims, int32_t batch, con
     launch_split(decode_hybrid_kernel, grid, s, a8, ax, pw.n_splits);
     if ((st = launch_status("decode_hybrid_kernel")) != AKV_OK) return st;
     return launch_combine(rows, dims->head_dim, a8.part_o, a8.part_lse, n_cols, out_o, out_lse, s);
+}
+
+extern "C" akv_status akv_decode_hybrid(const akv_dims* dims, int32_t batch, const uint16_t* q,
+                                        const int8_t* k_codes, const int8_t* v_codes, const float* k_chan,
+                                        const float* k_tok, const float* v_chan, const int32_t* page_table_int8,
+                                        const int32_t* n_pages_int8, int32_t max_pages_int8, const uint16_t* k_bf16,
+                                        const uint16_t* v_bf16, const int32_t* page_table_window,
+                                        const int32_t* window_len, int32_t max_pages_window, float softmax_scale,
+                                        float* out_o, float* out_lse, void* workspace, size_t workspace_bytes,
+                                        void* stream) {
+    clear_error();
+    return decode_hybrid_impl(dims, batch, q, k_codes, v_codes, k_chan, k_tok, v_chan, page_table_int8,
+                              n_pages_int8, max_pages_int8, k_bf16, v_bf16, page_table_window, window_len,
+                              max_pages_window, softmax_scale, out_o, out_lse, workspace, workspace_bytes, false,
+                              stream);
+}
+
+extern "C" akv_status akv_decode_hybrid_static(const akv_dims* dims, int32_t batch, const uint16_t* q,
+                                               const int8_t* k_codes, const int8_t* v_codes, const float* k_chan,
+                                               const float* k_tok, const float* v_chan,
+                                               const int32_t* page_table_int8, const int32_t* n_pages_int8,
+                                               int32_t max_pages_int8, const uint16_t* k_bf16,
+                                               const uint16_t* v_bf16, const int32_t* page_table_window,
+                                               const int32_t* window_len, int32_t max_pages_window,
+                                               float softmax_scale, float* out_o, float* out_lse, void* stream) {
+    clear_error();
+    return decode_hybrid_impl(dims, batch, q, k_codes, v_codes, k_chan, k_tok, v_chan, page_table_int8,
+                              n_pages_int8, max_pages_int8, k_bf16, v_bf16, page_table_window, window_len,
+                              max_pages_window, softmax_scale, out_o, out_lse, nullptr, 0, true, stream);
 }
 
 extern "C" akv_status akv_decode_attn_l13(const akv_dims* dims, int32_t batch, const uint16_t* q,
