@@ -11,6 +11,13 @@ hybrid step the same history is decoded all-BF16 (exact tier over every
 page), and the quantizer's throughput is measured separately (it runs off
 the decode path).
 
+The default run (ctx128k) also measures, in the same process and outside the
+headline's timed region: the 32K config and the batched config (one launch
+of 32 requests, 16 two-request launches, 32 one-request launches, all-BF16)
+at their real shapes; the host-staged mode from 8K to 128K next to the tier
+gate's transfer-model prediction; and, in the cpu_baseline leg, the float64
+oracle on the timed step's own inputs, whose outputs check every timed layer.
+
 Prints ONE JSON line (rank 0).  `value` is KV bytes read per second by the
 hybrid step; µs per step is in `ms_per_step` and `extra`.
 """
@@ -29,6 +36,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 PAGE_INT8_BYTES = 64 * 256 * 2 + 64 * 4 + 256 * 4 * 2  # codes K+V, k_tok, k_chan, v_chan = 35,072
 PAGE_BF16_BYTES = 64 * 256 * 2 * 2  # K+V = 65,536
+RING_SLOTS = (2, 4)  # ring slot counts the host-staged sweep measures (the first is the reported one)
 
 
 def log(*a):
@@ -101,134 +109,166 @@ def build_layers(w, device):
     return plan, layers, tables, qt_ms, len(src)
 
 
-def run_gpu(args, w):
+def timed_steps(fn, steps, warmup, stream):
+    """Average ms of `steps` calls of fn after `warmup` untimed ones, bracketed
+    by device synchronisation and HIP events on `stream`."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def split_kernel_us(B, fn, steps, calls_per_step, name, stream):
+    """Average duration of the split-K kernel of each decode call made through
+    entry point `name`, from HIP events the library records around that
+    kernel on `stream` (akv_set_profile_events)."""
+    import torch
+
+    evs = []
+    for _ in range(steps * calls_per_step):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        b.record(stream)
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    it = iter(evs)
+    orig = getattr(B, name)
+
+    def hooked(*a, **kw):
+        e0, e1 = next(it)
+        B.akv_set_profile_events(e0, e1)
+        try:
+            orig(*a, **kw)
+        finally:
+            B.akv_set_profile_events(None, None)
+    setattr(B, name, hooked)
+    try:
+        for _ in range(steps):
+            fn()
+    finally:
+        setattr(B, name, orig)
+    torch.cuda.synchronize()
+    d = [a.elapsed_time(b) * 1e3 for a, b in evs]
+    return sum(d) / len(d)
+
+
+class Resident:
+    """One workload's 16 layers resident in HBM, with the decode calls of one
+    step as closures (all on the current stream)."""
+
+    def __init__(self, w, device):
+        import torch
+
+        from quantized_paged_kv_akv_amd import binding as B
+        from quantized_paged_kv_akv_amd import configs
+
+        self.B, self.w, self.device = B, w, device
+        t0 = time.time()
+        self.plan, self.layers, self.T, self.qt_ms, self.n_quant = build_layers(w, device)
+        log(f"[bench] {w.name}: inputs resident in HBM after {time.time() - t0:.1f}s")
+        self.Hkv, self.G, self.D = w.num_kv_heads, w.group, w.head_dim
+        self.dims = B.dims(self.Hkv, self.G)
+        self.sigma = configs.SIGMA
+        T = self.T
+        self.m8, self.mw, self.mf = T["t8"].shape[1], T["tw"].shape[1], T["tf"].shape[1]
+        self.stream = torch.cuda.current_stream()
+        shape = (w.batch, w.num_q_heads)
+        self.out = [torch.empty(shape + (self.D,), device=device) for _ in range(w.layers)]
+        self.outl = [torch.empty(shape, device=device) for _ in range(w.layers)]
+        self.ws = torch.empty(max(16, max(B.akv_decode_workspace_bytes(self.dims, w.batch, m)
+                                          for m in (self.m8, self.mw, self.mf))), dtype=torch.uint8, device=device)
+        # sized for launches of the whole batch, of two requests and of one
+        self.wsh = torch.empty(max(16, max(B.akv_decode_hybrid_workspace_bytes(self.dims, k, self.m8, self.mw)
+                                           for k in {w.batch, min(2, w.batch), 1})),
+                               dtype=torch.uint8, device=device)
+        by = step_kv_bytes(self.plan, self.Hkv)
+        self.layer_bytes = by["int8"] + by["window"]
+        self.bf16_layer_bytes = by["bf16_all"]
+
+    def hybrid_step(self, k=None):
+        """One layer = akv_decode_hybrid (split-K kernel over int8 + window
+        pages, then the exact fold); with k, launches of k requests each."""
+        B, T, w = self.B, self.T, self.w
+        k = k or w.batch
+        for i, L in enumerate(self.layers):
+            for b0 in range(0, w.batch, k):
+                s = slice(b0, b0 + k)
+                B.akv_decode_hybrid(self.dims, k, L["q"][s], L["k_codes"], L["v_codes"], L["k_chan"], L["k_tok"],
+                                    L["v_chan"], T["t8"][s], T["n8"][s], self.m8, L["k_pool"], L["v_pool"],
+                                    T["tw"][s], T["nw"][s], self.mw, self.sigma, self.out[i][s], self.outl[i][s],
+                                    self.wsh, self.stream)
+
+    def bf16_step(self):
+        B, T = self.B, self.T
+        for i, L in enumerate(self.layers):
+            B.akv_decode_attn_exact(self.dims, self.w.batch, L["q"], L["k_pool"], L["v_pool"], T["tf"], T["nf"],
+                                    self.mf, self.sigma, self.out[i], self.outl[i], self.ws, self.stream)
+
+    def time_hybrid(self, steps, warmup):
+        ms = timed_steps(self.hybrid_step, steps, warmup, self.stream)
+        us = split_kernel_us(self.B, self.hybrid_step, max(2, steps // 2), self.w.layers * 1, "akv_decode_hybrid",
+                             self.stream)
+        return ms, us
+
+    def free(self):
+        import torch
+
+        self.layers.clear()
+        self.T.clear()
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
+
+def run_gpu(args, w, res):
+    """The headline workload: hybrid step (fused entry), the same layer as four
+    separate calls, all-BF16 exact decode, the 13-bit tier, single-step
+    spread and the streaming-read ceiling."""
     import torch
 
     from quantized_paged_kv_akv_amd import binding as B
-    from quantized_paged_kv_akv_amd import configs
 
-    device = torch.device("cuda", 0)
-    torch.cuda.set_device(device)
-    log(f"[bench] building {w.name}: {w.layers} layers, lengths {w.lengths[:4]}...")
-    t0 = time.time()
-    plan, layers, T, qt_ms, n_quant = build_layers(w, device)
-    log(f"[bench] inputs resident in HBM after {time.time() - t0:.1f}s")
-    Hkv, G, D = w.num_kv_heads, w.group, w.head_dim
-    dims = B.dims(Hkv, G)
-    batch = w.batch
+    device, stream = res.device, res.stream
+    layers, T, dims, sigma = res.layers, res.T, res.dims, res.sigma
+    Hkv, D, batch = res.Hkv, res.D, w.batch
     rows = batch * w.num_q_heads
-    sigma = configs.SIGMA
-    m8, mw, mf = T["t8"].shape[1], T["tw"].shape[1], T["tf"].shape[1]
-    ws = torch.empty(max(B.akv_decode_workspace_bytes(dims, batch, m) for m in (m8, mw, mf)), dtype=torch.uint8,
-                     device=device)
-    o8 = torch.empty((batch, w.num_q_heads, D), device=device)
-    l8 = torch.empty((batch, w.num_q_heads), device=device)
-    ow = torch.empty_like(o8)
-    lw = torch.empty_like(l8)
-    out = [torch.empty_like(o8) for _ in range(w.layers)]
-    outl = [torch.empty_like(l8) for _ in range(w.layers)]
-    stream = torch.cuda.current_stream()
+    m8, mw, mf = res.m8, res.mw, res.mf
+    out, outl, ws = res.out, res.outl, res.ws
+    o_w = torch.empty_like(out[0])
+    l_w = torch.empty_like(outl[0])
 
-    wsh = torch.empty(max(16, B.akv_decode_hybrid_workspace_bytes(dims, batch, m8, mw)), dtype=torch.uint8,
-                      device=device)
-
-    def hybrid_step():
-        # one layer = akv_decode_hybrid: split-K kernel over int8 + window pages, then the exact fold
-        for i, L in enumerate(layers):
-            B.akv_decode_hybrid(dims, batch, L["q"], L["k_codes"], L["v_codes"], L["k_chan"], L["k_tok"],
-                                L["v_chan"], T["t8"], T["n8"], m8, L["k_pool"], L["v_pool"], T["tw"], T["nw"], mw,
-                                sigma, out[i], outl[i], wsh, stream)
+    log("[bench] hybrid step (fused entry) warmup + timed")
+    ms_hybrid = timed_steps(res.hybrid_step, args.steps, args.warmup, stream)
+    # the timed step's outputs, kept for the oracle check
+    hyb_out = [(o.clone(), l.clone()) for o, l in zip(out, outl)]
+    hyb_us = split_kernel_us(B, res.hybrid_step, max(2, args.steps // 2), w.layers, "akv_decode_hybrid", stream)
 
     def four_call_step():
-        # the same layer as the four separate entry points (int8, exact, merge)
+        # the same layer as the separate entry points (int8, exact, merge)
         for i, L in enumerate(layers):
             B.akv_decode_attn_int8(dims, batch, L["q"], L["k_codes"], L["v_codes"], L["k_chan"], L["k_tok"],
                                    L["v_chan"], T["t8"], T["n8"], m8, sigma, out[i], outl[i], ws, stream)
             B.akv_decode_attn_exact(dims, batch, L["q"], L["k_pool"], L["v_pool"], T["tw"], T["nw"], mw, sigma,
-                                    ow, lw, ws, stream)
-            B.akv_merge_lse(rows, D, out[i], outl[i], ow, lw, stream)
+                                    o_w, l_w, ws, stream)
+            B.akv_merge_lse(rows, D, out[i], outl[i], o_w, l_w, stream)
 
-    def bf16_step():
-        for i, L in enumerate(layers):
-            B.akv_decode_attn_exact(dims, batch, L["q"], L["k_pool"], L["v_pool"], T["tf"], T["nf"], mf, sigma,
-                                    out[i], outl[i], ws, stream)
-
-    def timed(fn, steps, warmup):
-        for _ in range(warmup):
-            fn()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(steps):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / steps
-
-    def split_kernel_us(fn, steps, name):
-        """Average duration of the split-K kernel of each decode call (entry
-        point `name`), from HIP events the library records around that kernel
-        on `stream`."""
-        evs = []
-        for _ in range(steps):
-            for i in range(w.layers):
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record(stream)
-                b.record(stream)
-                evs.append((a, b))
-        torch.cuda.synchronize()
-        it = iter(evs)
-        orig = getattr(B, name)
-
-        def hooked(*args, **kw):
-            a, b = next(it)
-            B.akv_set_profile_events(a, b)
-            try:
-                orig(*args, **kw)
-            finally:
-                B.akv_set_profile_events(None, None)
-        setattr(B, name, hooked)
-        try:
-            for _ in range(steps):
-                fn()
-        finally:
-            setattr(B, name, orig)
-        torch.cuda.synchronize()
-        d = [a.elapsed_time(b) * 1e3 for a, b in evs]
-        return sum(d) / len(d)
-
-    log("[bench] hybrid step (fused entry) warmup + timed")
-    ms_hybrid = timed(hybrid_step, args.steps, args.warmup)
-    hyb_us = split_kernel_us(hybrid_step, max(2, args.steps // 2), "akv_decode_hybrid")
-    owners = {}
-    if batch > 1:
-        # the same step as launches of two requests (pairs with equal page
-        # counts, the two-owner form) and as one launch per request
-        wsp = torch.empty(max(16, B.akv_decode_hybrid_workspace_bytes(dims, 2, m8, mw)), dtype=torch.uint8,
-                          device=device)
-
-        def rows_step(k):
-            def step():
-                for i, L in enumerate(layers):
-                    for b0 in range(0, batch, k):
-                        B.akv_decode_hybrid(dims, k, L["q"][b0:b0 + k], L["k_codes"], L["v_codes"], L["k_chan"],
-                                            L["k_tok"], L["v_chan"], T["t8"][b0:b0 + k], T["n8"][b0:b0 + k], m8,
-                                            L["k_pool"], L["v_pool"], T["tw"][b0:b0 + k], T["nw"][b0:b0 + k], mw,
-                                            sigma, out[i][b0:b0 + k], outl[i][b0:b0 + k], wsp, stream)
-            return step
-        log("[bench] two-owner and one-row steps")
-        owners = dict(ms_pairs=timed(rows_step(2), max(2, args.steps // 4), 1),
-                      ms_single=timed(rows_step(1), max(2, args.steps // 4), 1))
     log("[bench] four-call step")
-    ms_four = timed(four_call_step, max(2, args.steps // 2), 1)
+    ms_four = timed_steps(four_call_step, max(2, args.steps // 2), 1, stream)
     log("[bench] all-BF16 step")
-    ms_bf16 = timed(bf16_step, max(2, args.steps // 2), 1)
-    bf16_us = split_kernel_us(bf16_step, 2, "akv_decode_attn_exact")
+    ms_bf16 = timed_steps(res.bf16_step, max(2, args.steps // 2), 1, stream)
+    bf16_us = split_kernel_us(B, res.bf16_step, 2, w.layers, "akv_decode_attn_exact", stream)
 
     # lossless 13-bit tier, HBM-resident: each layer's whole history encoded
     # (akv_l13_encode_pages), then decoded directly by akv_decode_attn_l13
     log("[bench] lossless 13-bit tier: encode every layer, then the all-13-bit step")
-    l13_enc_ms, l13_read = [], 0
+    l13_enc_ms = []
     for L in layers:
         n = L["k_pool"].shape[0]
         sz = B.l13_sizes(dims, n)
@@ -256,13 +296,13 @@ def run_gpu(args, w):
             B.akv_decode_attn_l13(dims, batch, L["q"], L["l13"]["arena"], L["l13"]["desc"], L["l13"]["table"],
                                   T["tf"], T["nf"], mf, sigma, out[i], outl[i], ws, stream)
 
-    ms_l13 = timed(l13_step, max(2, args.steps // 2), 1)
-    l13_us = split_kernel_us(l13_step, 2, "akv_decode_attn_l13")
+    ms_l13 = timed_steps(l13_step, max(2, args.steps // 2), 1, stream)
+    l13_us = split_kernel_us(B, l13_step, 2, w.layers, "akv_decode_attn_l13", stream)
     l13_enc = sorted(l13_enc_ms)[len(l13_enc_ms) // 2]
     lossless = dict(ms_step=ms_l13, launch_us=l13_us, bytes_per_launch=l13_layer_bytes,
-                    arena_bytes_per_layer=l13_arena[0], arena_frac_of_bf16=l13_arena[0] / by_layer_bf16(plan, Hkv),
+                    arena_bytes_per_layer=l13_arena[0], arena_frac_of_bf16=l13_arena[0] / res.bf16_layer_bytes,
                     raw_planes=l13_raw, planes=n_planes * w.layers, encode_ms_per_layer=l13_enc,
-                    encode_GBps_in=by_layer_bf16(plan, Hkv) / (l13_enc * 1e-3) / 1e9)
+                    encode_GBps_in=res.bf16_layer_bytes / (l13_enc * 1e-3) / 1e9)
     for L in layers:
         del L["l13"]
     torch.cuda.empty_cache()
@@ -272,7 +312,7 @@ def run_gpu(args, w):
     for _ in range(max(10, args.steps)):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        hybrid_step()
+        res.hybrid_step()
         e1.record(stream)
         e1.synchronize()
         step_us.append(e0.elapsed_time(e1) * 1e3)
@@ -296,17 +336,47 @@ def run_gpu(args, w):
     read_gbps = 5 * (big.numel() // 32768 * 32768) / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del big
 
-    by = step_kv_bytes(plan, Hkv)
-    layer_bytes = by["int8"] + by["window"]
-    hybrid_bytes = layer_bytes * w.layers
-    bf16_bytes = by["bf16_all"] * w.layers
-    quant_ms = sum(qt_ms[1:]) / max(1, len(qt_ms) - 1) if len(qt_ms) > 1 else qt_ms[0]
-    quant_bytes = n_quant * Hkv * (PAGE_BF16_BYTES + PAGE_INT8_BYTES)
-    return dict(step_p=(pct(0.1), pct(0.5), pct(0.9)), read_gbps=read_gbps, owners=owners, ms_hybrid=ms_hybrid, ms_four=ms_four, ms_bf16=ms_bf16, hybrid_bytes=hybrid_bytes,
-                bf16_bytes=bf16_bytes, hyb_launch_us=hyb_us, hyb_bytes_per_launch=layer_bytes,
-                hyb_achieved_gbps=layer_bytes / (hyb_us * 1e-6) / 1e9,
-                bf16_launch_us=bf16_us, bf16_achieved_gbps=by["bf16_all"] / (bf16_us * 1e-6) / 1e9,
-                quant_ms_per_layer=quant_ms, quant_gbps=quant_bytes / (quant_ms * 1e-3) / 1e9, lossless=lossless)
+    quant_ms = sum(res.qt_ms[1:]) / max(1, len(res.qt_ms) - 1) if len(res.qt_ms) > 1 else res.qt_ms[0]
+    quant_bytes = res.n_quant * Hkv * (PAGE_BF16_BYTES + PAGE_INT8_BYTES)
+    return dict(step_p=(pct(0.1), pct(0.5), pct(0.9)), read_gbps=read_gbps, ms_hybrid=ms_hybrid,
+                ms_four=ms_four, ms_bf16=ms_bf16, hybrid_bytes=res.layer_bytes * w.layers,
+                bf16_bytes=res.bf16_layer_bytes * w.layers, hyb_launch_us=hyb_us,
+                hyb_bytes_per_launch=res.layer_bytes, hyb_achieved_gbps=res.layer_bytes / (hyb_us * 1e-6) / 1e9,
+                bf16_launch_us=bf16_us, bf16_achieved_gbps=res.bf16_layer_bytes / (bf16_us * 1e-6) / 1e9,
+                quant_ms_per_layer=quant_ms, quant_gbps=quant_bytes / (quant_ms * 1e-3) / 1e9, lossless=lossless,
+                hyb_out=hyb_out)
+
+
+def run_config(args, w, owner_modes=False):
+    """A further workload at its real shape: the hybrid step (one launch per
+    layer), its split kernel, and for batched workloads the same step as
+    two-request (two-owner) launches and as one launch per request, plus the
+    all-BF16 step."""
+    import torch
+
+    device = torch.device("cuda", 0)
+    res = Resident(w, device)
+    steps = max(4, args.steps // 2)
+    ms, us = res.time_hybrid(steps, max(1, args.warmup // 2))
+    out = dict(us_per_step=round(ms * 1e3, 2), us_per_layer=round(ms * 1e3 / w.layers, 2),
+               kv_bytes_per_step=res.layer_bytes * w.layers,
+               GBps_step=round(res.layer_bytes * w.layers / (ms * 1e-3) / 1e9, 1),
+               frac_of_hbm_peak_step=round(res.layer_bytes * w.layers / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+               split_kernel_us=round(us, 2), split_kernel_GBps=round(res.layer_bytes / (us * 1e-6) / 1e9, 1),
+               requests=w.batch, context_tokens=[int(x) for x in w.lengths])
+    if owner_modes:
+        log(f"[bench] {w.name}: two-owner and one-row launches, all-BF16 step")
+        ms2 = timed_steps(lambda: res.hybrid_step(2), max(2, steps // 2), 1, res.stream)
+        ms1 = timed_steps(lambda: res.hybrid_step(1), max(2, steps // 4), 1, res.stream)
+        msb = timed_steps(res.bf16_step, max(2, steps // 2), 1, res.stream)
+        out.update(us_per_step_two_owner_launches=round(ms2 * 1e3, 2),
+                   us_per_step_one_row_launches=round(ms1 * 1e3, 2),
+                   us_per_step_bf16_all=round(msb * 1e3, 2),
+                   bf16_kv_bytes_per_step=res.bf16_layer_bytes * w.layers,
+                   hybrid_speedup_vs_bf16=round(msb / ms, 3),
+                   two_owner_vs_one_row_time=round(ms2 / ms1, 3))
+    res.free()
+    return out
 
 
 def by_layer_bf16(plan, Hkv) -> int:
@@ -314,14 +384,16 @@ def by_layer_bf16(plan, Hkv) -> int:
     return step_kv_bytes(plan, Hkv)["bf16_all"]
 
 
-def run_staged(args, w):
+def run_staged(args, w, with_l13=True, ring_slots=(2,)):
     """Host-staged step: each layer's history sits in pinned host memory and
     is staged into a two-slot device ring on a side stream (events guard slot
     reuse), overlapped with the previous layer's attention.  The hybrid step
     stages the int8 pool (codes + scales) and the BF16 window pages; the
     all-BF16 step stages the whole BF16 pool; the lossless step stages the
     whole history in the 13-bit format (packed planes, descriptors, tables)
-    and decodes it with akv_decode_attn_l13."""
+    and decodes it with akv_decode_attn_l13.  Before the history leaves HBM,
+    the same hybrid and all-BF16 steps are timed HBM-resident (the per-layer
+    decode times the tier gate's transfer model needs)."""
     import torch
 
     from quantized_paged_kv_akv_amd import binding as B
@@ -330,11 +402,16 @@ def run_staged(args, w):
     device = torch.device("cuda", 0)
     torch.cuda.set_device(device)
     log(f"[bench] building {w.name}: {w.layers} layers, lengths {w.lengths[:4]}...")
-    plan, layers, T, _, _ = build_layers(w, device)
+    res = Resident(w, device)
+    plan, layers, T = res.plan, res.layers, res.T
     Hkv, G = w.num_kv_heads, w.group
     dims = B.dims(Hkv, G)
     sigma = configs.SIGMA
     m8, mw, mf = T["t8"].shape[1], T["tw"].shape[1], T["tf"].shape[1]
+    comp = torch.cuda.current_stream()
+    # HBM-resident decode time per layer of each tier
+    res_h = timed_steps(res.hybrid_step, 4, 2, comp) / w.layers
+    res_b = timed_steps(res.bf16_step, 4, 2, comp) / w.layers
     tw_c = torch.arange(T["tw"].numel(), dtype=torch.int32, device=device).view(T["tw"].shape)
     widx = T["tw"].reshape(-1).long()
 
@@ -357,87 +434,100 @@ def run_staged(args, w):
             blk[o:o + n].copy_(t.contiguous().view(-1).view(torch.uint8))
         return blk, [(o, t.dtype, tuple(t.shape)) for t, o in zip(ts, offs)]
 
-    log("[bench] encoding the 13-bit history and copying everything to pinned host memory")
+    log("[bench] copying the history to pinned host memory" + (" (and encoding it 13-bit)" if with_l13 else ""))
     host_h, host_b, host_l, lay_h, lay_l = [], [], [], None, []
     n_slots = layers[0]["k_pool"].shape[0]
-    sz = B.l13_sizes(dims, n_slots)
-    l13_arena = torch.empty(sz["arena_bytes"], dtype=torch.uint8, device=device)
-    l13_desc = torch.empty(sz["desc"], dtype=torch.int32, device=device)
-    l13_table = torch.empty(sz["table"], dtype=torch.uint8, device=device)
-    l13_end = torch.empty(1, dtype=torch.int64, device=device)
-    all_slots = torch.arange(n_slots, dtype=torch.int32, device=device)
+    if with_l13:
+        sz = B.l13_sizes(dims, n_slots)
+        l13_arena = torch.empty(sz["arena_bytes"], dtype=torch.uint8, device=device)
+        l13_desc = torch.empty(sz["desc"], dtype=torch.int32, device=device)
+        l13_table = torch.empty(sz["table"], dtype=torch.uint8, device=device)
+        l13_end = torch.empty(1, dtype=torch.int64, device=device)
+        all_slots = torch.arange(n_slots, dtype=torch.int32, device=device)
     for L in layers:
         blk, lay_h = packed([L[k] for k in ("k_codes", "v_codes", "k_chan", "k_tok", "v_chan")]
                             + [L["k_pool"][widx], L["v_pool"][widx]])
         host_h.append([blk])
         host_b.append([pinned(L["k_pool"]), pinned(L["v_pool"])])
-        B.akv_l13_encode_pages(dims, n_slots, L["k_pool"], L["v_pool"], all_slots, all_slots, l13_arena, 0,
-                               l13_desc, l13_table, l13_end)
-        end = int(l13_end[0])
-        blk, lay = packed([l13_arena[:end], l13_desc, l13_table])
-        host_l.append([blk])
-        lay_l.append(lay)
+        if with_l13:
+            B.akv_l13_encode_pages(dims, n_slots, L["k_pool"], L["v_pool"], all_slots, all_slots, l13_arena, 0,
+                                   l13_desc, l13_table, l13_end)
+            end = int(l13_end[0])
+            blk, lay = packed([l13_arena[:end], l13_desc, l13_table])
+            host_l.append([blk])
+            lay_l.append(lay)
         for k in ("k_codes", "v_codes", "k_chan", "k_tok", "v_chan", "k_pool", "v_pool"):
             del L[k]
-    del l13_arena
+    if with_l13:
+        del l13_arena
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
 
     def nbytes(srcs):
         return sum((t.numel() * t.element_size() + 255) // 256 * 256 for t in srcs)
 
-    bytes_h = sum(torch.Size(shp).numel() * torch.empty((), dtype=dt).element_size() for _, dt, shp in lay_h) * w.layers
+    def tbytes(lay):
+        return sum(torch.Size(shp).numel() * torch.empty((), dtype=dt).element_size() for _, dt, shp in lay)
+
+    bytes_h = tbytes(lay_h) * w.layers
     bytes_b = sum(t.numel() * t.element_size() for t in host_b[0]) * w.layers
-    bytes_l = sum(sum(torch.Size(shp).numel() * torch.empty((), dtype=dt).element_size() for _, dt, shp in lay)
-                  for lay in lay_l)
-    ring_h = B.Ring([torch.empty(nbytes(host_h[0]), dtype=torch.uint8, device=device) for _ in range(2)])
-    ring_b = B.Ring([torch.empty(nbytes(host_b[0]), dtype=torch.uint8, device=device) for _ in range(2)])
-    ring_l = B.Ring([torch.empty(max(nbytes(h) for h in host_l), dtype=torch.uint8, device=device)
-                     for _ in range(2)])
+    bytes_l = sum(tbytes(lay) for lay in lay_l)
+    n_ring = max(ring_slots)
+    ring_h = B.Ring([torch.empty(nbytes(host_h[0]), dtype=torch.uint8, device=device) for _ in range(n_ring)])
+    ring_b = B.Ring([torch.empty(nbytes(host_b[0]), dtype=torch.uint8, device=device) for _ in range(n_ring)])
+    ring_l = (B.Ring([torch.empty(max(nbytes(h) for h in host_l), dtype=torch.uint8, device=device)
+                      for _ in range(2)]) if with_l13 else None)
+    # rings of fewer slots reuse the first slots' memory (only one ring is in use at a time)
+    rings_h = {k: (ring_h if k == n_ring else B.Ring(ring_h.slots[:k])) for k in ring_slots}
+    rings_b = {k: (ring_b if k == n_ring else B.Ring(ring_b.slots[:k])) for k in ring_slots}
     copy_s = torch.cuda.Stream()
-    comp = torch.cuda.current_stream()
     out = torch.empty((w.batch, w.num_q_heads, w.head_dim), device=device)
     outl = torch.empty((w.batch, w.num_q_heads), device=device)
-    wsh = torch.empty(max(16, B.akv_decode_hybrid_workspace_bytes(dims, w.batch, m8, mw)), dtype=torch.uint8,
-                      device=device)
-    wsb = torch.empty(max(16, B.akv_decode_workspace_bytes(dims, w.batch, mf)), dtype=torch.uint8, device=device)
+    wsh, wsb = res.wsh, torch.empty(max(16, B.akv_decode_workspace_bytes(dims, w.batch, mf)), dtype=torch.uint8,
+                                    device=device)
+
+    def views(slot, lay):
+        return [slot[o:o + torch.Size(shp).numel() * torch.empty((), dtype=dt).element_size()].view(dt).view(shp)
+                for o, dt, shp in lay]
+
+    # device views of each ring slot, made once (the per-layer host work is
+    # then the staging call, the decode call and the release call)
+    views_h = {t.data_ptr(): views(t, lay_h) for t in ring_h.slots}
+    views_b = {}
+    for t in ring_b.slots:
+        off, vs = 0, []
+        for h in host_b[0]:
+            n = h.numel() * h.element_size()
+            vs.append(t[off:off + n].view(h.dtype).view(h.shape))
+            off += (n + 255) // 256 * 256
+        views_b[t.data_ptr()] = vs
+    q_l = [L["q"] for L in layers]
+
+    cur = dict(h=ring_h, b=ring_b)
 
     def hybrid_step():
-        for i, L in enumerate(layers):
-            slot = ring_h.stage_views(i, host_h[i], copy_s, comp)[0]
-            v = [slot[o:o + torch.Size(shp).numel() * torch.empty((), dtype=dt).element_size()].view(dt).view(shp)
-                 for o, dt, shp in lay_h]
-            B.akv_decode_hybrid(dims, w.batch, L["q"], v[0], v[1], v[2], v[3], v[4], T["t8"], T["n8"], m8, v[5],
+        rh = cur["h"]._h
+        for i in range(w.layers):
+            v = views_h[B.akv_ring_stage(rh, i, host_h[i], copy_s, comp)[0]]
+            B.akv_decode_hybrid(dims, w.batch, q_l[i], v[0], v[1], v[2], v[3], v[4], T["t8"], T["n8"], m8, v[5],
                                 v[6], tw_c, T["nw"], mw, sigma, out, outl, wsh, comp)
-            ring_h.release(i, comp)
+            B.akv_ring_release(rh, i, comp)
 
     def bf16_step():
-        for i, L in enumerate(layers):
-            v = ring_b.stage_views(i, host_b[i], copy_s, comp)
-            B.akv_decode_attn_exact(dims, w.batch, L["q"], v[0], v[1], T["tf"], T["nf"], mf, sigma, out, outl,
+        rb = cur["b"]._h
+        for i in range(w.layers):
+            v = views_b[B.akv_ring_stage(rb, i, host_b[i], copy_s, comp)[0]]
+            B.akv_decode_attn_exact(dims, w.batch, q_l[i], v[0], v[1], T["tf"], T["nf"], mf, sigma, out, outl,
                                     wsb, comp)
-            ring_b.release(i, comp)
+            B.akv_ring_release(rb, i, comp)
 
     def l13_step():
-        for i, L in enumerate(layers):
+        for i in range(w.layers):
             slot = ring_l.stage_views(i, host_l[i], copy_s, comp)[0]
-            v = [slot[o:o + torch.Size(shp).numel() * torch.empty((), dtype=dt).element_size()].view(dt).view(shp)
-                 for o, dt, shp in lay_l[i]]
-            B.akv_decode_attn_l13(dims, w.batch, L["q"], v[0], v[1], v[2], T["tf"], T["nf"], mf, sigma, out, outl,
+            v = views(slot, lay_l[i])
+            B.akv_decode_attn_l13(dims, w.batch, q_l[i], v[0], v[1], v[2], T["tf"], T["nf"], mf, sigma, out, outl,
                                   wsb, comp)
             ring_l.release(i, comp)
-
-    def timed(fn, steps, warmup):
-        for _ in range(warmup):
-            fn()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(comp)
-        for _ in range(steps):
-            fn()
-        e1.record(comp)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / steps
 
     # plain host-to-device copy rate of one layer's BF16 pool, for reference
     big = host_b[0][0]
@@ -454,24 +544,50 @@ def run_staged(args, w):
     h2d_gbps = 5 * big.numel() * big.element_size() / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del dst
 
-    # one untimed pass of every mode first: the first staged mode timed on a
-    # fresh process otherwise runs up to 15% slower (host-to-device copies
-    # ramp up over the first few hundred milliseconds of sustained traffic)
-    for fn in (hybrid_step, bf16_step, l13_step):
+    # untimed passes of every mode first, at least half a second of sustained
+    # copies: the first staged mode timed otherwise runs up to 15% slower
+    # (host-to-device copy rates ramp up over the first few hundred
+    # milliseconds of traffic)
+    modes = (hybrid_step, bf16_step, l13_step) if with_l13 else (hybrid_step, bf16_step)
+    t_warm = time.time()
+    while True:
+        for fn in modes:
+            fn()
+        torch.cuda.synchronize()
+        if time.time() - t_warm > 0.5:
+            break
+    # host time to enqueue one step (16 x stage, decode, release), GPU idle
+    enq = {}
+    for name, fn in (("hybrid", hybrid_step), ("exact", bf16_step)):
+        torch.cuda.synchronize()
+        t_h = time.perf_counter()
         fn()
-    torch.cuda.synchronize()
-    log("[bench] staged hybrid step")
+        enq[name] = (time.perf_counter() - t_h) * 1e3
+        torch.cuda.synchronize()
     steps = max(2, args.steps // 4)
-    ms_h = timed(hybrid_step, steps, 1)
-    log("[bench] staged all-BF16 step")
-    ms_b = timed(bf16_step, steps, 1)
-    log("[bench] staged lossless 13-bit step")
-    ms_l = timed(l13_step, steps, 1)
+    by_slots = {}
+    for k in ring_slots:
+        cur["h"], cur["b"] = rings_h[k], rings_b[k]
+        log(f"[bench] {w.name}: staged hybrid and all-BF16 steps, {k}-slot ring")
+        by_slots[k] = dict(ms_h=timed_steps(hybrid_step, steps, 1, comp), ms_b=timed_steps(bf16_step, steps, 1, comp))
+    ms_h, ms_b = by_slots[ring_slots[0]]["ms_h"], by_slots[ring_slots[0]]["ms_b"]
+    for k in ring_slots:
+        if k != n_ring:
+            rings_h[k].destroy()
+            rings_b[k].destroy()
+    ms_l = None
+    if with_l13:
+        log(f"[bench] {w.name}: staged lossless 13-bit step")
+        ms_l = timed_steps(l13_step, steps, 1, comp)
+        ring_l.destroy()
     ring_h.destroy()
     ring_b.destroy()
-    ring_l.destroy()
+    res.free()
     return dict(ms_h=ms_h, ms_b=ms_b, ms_l=ms_l, bytes_h=bytes_h, bytes_b=bytes_b, bytes_l=bytes_l,
-                h2d_gbps=h2d_gbps, steps=steps)
+                h2d_gbps=h2d_gbps, steps=steps, resident_ms_per_layer=dict(hybrid=res_h, exact=res_b),
+                host_enqueue_ms=enq, by_slots=by_slots,
+                copies_per_layer=dict(hybrid=[nbytes(host_h[0])],
+                                      exact=[t.numel() * t.element_size() for t in host_b[0]]))
 
 
 def pcie_curve(sizes_mib=(0.0625, 0.25, 1, 4, 16, 64, 256, 512)):
@@ -501,77 +617,195 @@ def pcie_curve(sizes_mib=(0.0625, 0.25, 1, 4, 16, 64, 256, 512)):
     return out
 
 
-def staged_sweep(args):
-    """Host-staged per-token time against context length, exact (all-BF16)
-    against hybrid, and the tier the measured times choose at each length."""
+def staged_copy_curve(sizes_mib=(1, 4, 8, 16, 32, 64, 128, 256), n_slots=2):
+    """Host-to-device copy time against size in the staging pattern itself:
+    one copy per "layer" through an n_slots akv ring (each copy waits for the
+    compute stream to release the slot it overwrites, the compute stream
+    waits for each copy), with no kernel in between.  This is the bus
+    behaviour the staged step sees, dependencies included; plain
+    back-to-back copies (pcie_curve) overlap consecutive transfers and read
+    faster for sizes around 10-30 MB."""
+    import torch
+
+    from quantized_paged_kv_akv_amd import binding as B
+
+    device = torch.device("cuda", 0)
+    big = torch.empty(int(max(sizes_mib) * (1 << 20)), dtype=torch.uint8, pin_memory=True)
+    copy_s, comp = torch.cuda.Stream(), torch.cuda.current_stream()
+    out = []
+    for mib in sizes_mib:
+        n = int(mib * (1 << 20))
+        src = [big[:n]]
+        ring = B.Ring([torch.empty(n, dtype=torch.uint8, device=device) for _ in range(n_slots)])
+        reps = max(8, min(128, int(2048 / mib)))
+
+        def run(k):
+            for i in range(k):
+                B.akv_ring_stage(ring._h, i, src, copy_s, comp)
+                B.akv_ring_release(ring._h, i, comp)
+
+        t_warm = time.time()
+        while time.time() - t_warm < 0.2:
+            run(8)
+            torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(comp)
+        run(reps)
+        e1.record(comp)
+        torch.cuda.synchronize()
+        out.append((mib, reps * n / (e0.elapsed_time(e1) * 1e-3) / 1e9))
+        ring.destroy()
+    return out
+
+
+def staged_sweep(args, contexts=(8192, 16384, 32768, 65536, 131072), with_l13=False):
+    """Host-staged per-token time against context length, hybrid against
+    exact (all-BF16) (and the 13-bit tier if asked), next to the tier gate's
+    prediction: a copy-time model t(n) = latency + n / bandwidth fitted to
+    the measured host-to-device curve, fed each tier's per-layer copy sizes
+    and its HBM-resident decode time, through the two-slot staging
+    schedule.  The gate picks the tier with the smallest predicted time."""
     import gc
 
     import torch
 
     from quantized_paged_kv_akv_amd import inputs
+    from quantized_paged_kv_akv_amd import tier_gate as TG
 
-    rows = []
-    for L in (8192, 16384, 32768, 65536, 131072):
+    curve = pcie_curve()
+    copy = TG.fit_copy_model([m * (1 << 20) for m, _ in curve], [g * 1e9 for _, g in curve])
+    scurve = {ns: staged_copy_curve(n_slots=ns) for ns in RING_SLOTS}
+    model = TG.fit_staging_model(copy, {ns: ([m * (1 << 20) for m, _ in c], [g * 1e9 for _, g in c])
+                                        for ns, c in scurve.items()})
+    log(f"[bench] copy model: latency {copy.latency_s * 1e6:.1f} us, bandwidth {copy.bandwidth_Bps / 1e9:.1f} GB/s; "
+        f"through the ring: {model.stage_overhead_s * 1e6:.1f} us per layer, round trip "
+        f"{model.round_trip_s * 1e6:.0f} us")
+    rows, last = [], None
+    for L in contexts:
         w = inputs.Workload(f"staged{L // 1024}k", 4, batch=1, layers=16, num_kv_heads=4, group=6, lengths=(L,),
                             window=1024, outlier_frac=0.02, permute=False)
-        r = run_staged(args, w)
-        times = {"hybrid": r["ms_h"], "exact": r["ms_b"], "lossless13": r["ms_l"]}
-        rows.append(dict(context=L, ms_hybrid=round(r["ms_h"], 3), ms_bf16=round(r["ms_b"], 3),
-                         ms_lossless13=round(r["ms_l"], 3),
-                         bytes_hybrid=r["bytes_h"], bytes_bf16=r["bytes_b"], bytes_lossless13=r["bytes_l"],
-                         pcie_GBps_hybrid=round(r["bytes_h"] / (r["ms_h"] * 1e-3) / 1e9, 1),
-                         pcie_GBps_bf16=round(r["bytes_b"] / (r["ms_b"] * 1e-3) / 1e9, 1),
-                         pcie_GBps_lossless13=round(r["bytes_l"] / (r["ms_l"] * 1e-3) / 1e9, 1),
-                         chosen=min(times, key=times.get),
-                         chosen_lossless_only="lossless13" if r["ms_l"] < r["ms_b"] else "exact"))
-        log(f"[bench] {w.name}: hybrid {r['ms_h']:.2f} ms, exact {r['ms_b']:.2f} ms, "
-            f"lossless13 {r['ms_l']:.2f} ms")
+        r = run_staged(args, w, with_l13=with_l13, ring_slots=RING_SLOTS)
+        kern = {k: v * 1e-3 for k, v in r["resident_ms_per_layer"].items()}
+        row = dict(context=L)
+        for ns in RING_SLOTS:
+            meas = {"hybrid": r["by_slots"][ns]["ms_h"], "exact": r["by_slots"][ns]["ms_b"]}
+            pred = {k: v * 1e3 for k, v in TG.predict(model, r["copies_per_layer"], kern, layers=w.layers,
+                                                      n_slots=ns).items()}
+            row[f"slots{ns}"] = dict(
+                ms_hybrid=round(meas["hybrid"], 3), ms_bf16=round(meas["exact"], 3),
+                predicted_ms_hybrid=round(pred["hybrid"], 3), predicted_ms_bf16=round(pred["exact"], 3),
+                prediction_error_hybrid=round(pred["hybrid"] / meas["hybrid"] - 1, 4),
+                prediction_error_bf16=round(pred["exact"] / meas["exact"] - 1, 4),
+                chosen_by_model=TG.choose(pred), chosen_by_measurement=min(meas, key=meas.get))
+        row.update(ms_hybrid=round(r["ms_h"], 3), ms_bf16=round(r["ms_b"], 3),
+                   resident_us_per_layer_hybrid=round(r["resident_ms_per_layer"]["hybrid"] * 1e3, 2),
+                   resident_us_per_layer_bf16=round(r["resident_ms_per_layer"]["exact"] * 1e3, 2),
+                   bytes_hybrid=r["bytes_h"], bytes_bf16=r["bytes_b"],
+                   pcie_GBps_hybrid=round(r["bytes_h"] / (r["ms_h"] * 1e-3) / 1e9, 1),
+                   pcie_GBps_bf16=round(r["bytes_b"] / (r["ms_b"] * 1e-3) / 1e9, 1),
+                   h2d_copy_GBps=round(r["h2d_gbps"], 1),
+                   host_enqueue_ms_hybrid=round(r["host_enqueue_ms"]["hybrid"], 3),
+                   host_enqueue_ms_bf16=round(r["host_enqueue_ms"]["exact"], 3))
+        if with_l13:
+            row.update(ms_lossless13=round(r["ms_l"], 3), bytes_lossless13=r["bytes_l"],
+                       pcie_GBps_lossless13=round(r["bytes_l"] / (r["ms_l"] * 1e-3) / 1e9, 1))
+        rows.append(row)
+        for ns in RING_SLOTS:
+            x = row[f"slots{ns}"]
+            log(f"[bench] {w.name} {ns} slots: hybrid {x['ms_hybrid']:.2f} ms (model {x['predicted_ms_hybrid']:.2f}), "
+                f"exact {x['ms_bf16']:.2f} ms (model {x['predicted_ms_bf16']:.2f})")
+        last = r
         gc.collect()
         torch.cuda.empty_cache()
-    return rows
+    return dict(curve=curve, staged_curve=scurve, model=model, rows=rows, last=last)
 
 
-def cpu_baseline(w):
-    """The float64 oracle, as it stands, on a bounded sample of the workload:
-    64 independent (request, KV head) units at this context length -- as many
-    units as one 16-layer step of 4 KV heads -- all reading one KV head's
-    pages (int8-path formula over the old pages, exact window, LSE merge).
-    Scaled to µs per full decode step."""
+def staging_model_json(m) -> dict:
+    return {"latency_us": round(m.copy.latency_s * 1e6, 2), "bandwidth_GBps": round(m.copy.bandwidth_Bps / 1e9, 2),
+            "fitted_to": "pcie_h2d_curve (plain back-to-back copies)",
+            "ring_overhead_us_per_layer": round(m.stage_overhead_s * 1e6, 2),
+            "ring_round_trip_us": round(m.round_trip_s * 1e6, 1),
+            "ring_terms_fitted_to": "staged_copy_curve (copies through the ring, no kernel, each slot count)"}
+
+
+def tile_order_to_token_major(a):
+    """Key codes in the library's tile order (include/akv.h: K[t][d] of a
+    page-head at byte ((4 (d / 64) + (t / 4) % 4) * 64 + 16 ((d / 16) % 4) +
+    4 (t / 16) + t % 4) * 16 + d % 16), given as [..., 4, 4, 4, 4, 4, 16]
+    (d / 64, (t / 4) % 4, (d / 16) % 4, t / 16, t % 4, d % 16), returned
+    token-major [..., t / 16, (t / 4) % 4, t % 4, d / 64, (d / 16) % 4, d % 16]
+    = [..., 64, 256] (a transpose)."""
     import numpy as np
 
-    from oracle import oracle as O
-    from quantized_paged_kv_akv_amd import configs, inputs
+    n = a.ndim - 6
+    lead = tuple(range(n))
+    return np.ascontiguousarray(a.transpose(lead + (n + 3, n + 1, n + 4, n, n + 2, n + 5)))
 
-    units = 64
-    w1 = inputs.Workload(w.name + "-1head", w.cfg_id, batch=1, layers=1, num_kv_heads=1, group=w.group,
-                         lengths=w.lengths[:1], window=w.window, outlier_frac=w.outlier_frac, permute=False)
+
+def cpu_baseline(w, res, hyb_out):
+    """The float64 oracle, as it stands, on the timed step's own inputs: all
+    64 (layer, KV head) units of one 16-layer decode step, each reading its
+    own layer's int8 pages (int8-path formula) and BF16 window pages (exact),
+    then the LSE merge -- timed on the host's cores.  Its outputs are the
+    oracle check of the timed hybrid step: every layer's O and LSE against
+    the GPU's, at the acceptance tolerances."""
+    import numpy as np
+    import torch
+
+    from oracle import oracle as O
+
+    def bits(t):
+        """BF16 device tensor -> uint16 host array of its bit patterns."""
+        return t.view(dtype=torch.int16).cpu().numpy().view(np.uint16)
+
     t0 = time.time()
-    d = inputs.make_layer_np(w1, 0)
-    plan = d["plan"]
-    src, dst = plan.quant_src_dst()
-    qz = O.quantize_pages(d["k_pool"], d["v_pool"], src, dst, plan.int8_slots_total, 1)
-    log(f"[bench] cpu baseline sample prepared in {time.time() - t0:.1f}s")
-    q = np.repeat(d["q"], units, axis=0)
-    t8 = np.repeat(plan.int8_table(), units, axis=0)
-    tw = np.repeat(plan.window_table(), units, axis=0)
-    n8 = np.full(units, plan.n8[0], np.int32)
-    nw = np.full(units, plan.win_tokens[0], np.int32)
+    plan, T, Hkv, G, D = res.plan, res.T, res.Hkv, res.G, res.D
+    nl = w.layers
+    t8 = plan.int8_table()
+    tw = plan.window_table()
+    n8 = int(plan.n8[0])
+    wp = tw.shape[1]
+    # one pool holding every layer's pages: layer i's int8 pages at slots
+    # [i n8, (i + 1) n8), its window pages at [i wp, (i + 1) wp)
+    kc = np.empty((nl * n8, Hkv, 64, 256), np.int8)
+    vc = np.empty((nl * n8, Hkv, 256, 64), np.int8)
+    kch = np.empty((nl * n8, Hkv, 256), np.float32)
+    ktk = np.empty((nl * n8, Hkv, 64), np.float32)
+    vch = np.empty((nl * n8, Hkv, 256), np.float32)
+    kw = np.empty((nl * wp, Hkv, 64, 256), np.uint16)
+    vw = np.empty((nl * wp, Hkv, 256, 64), np.uint16)
+    q = np.empty((nl, Hkv * G, D), np.uint16)
+    sl8 = t8[0, :n8].astype(np.int64)
+    slw = tw[0].astype(np.int64)
+    ident = bool(np.array_equal(sl8, np.arange(n8)))
+
+    def rows_of(t):
+        a = t.cpu().numpy()
+        return a[:n8] if ident else a[sl8]
+
+    for i, L in enumerate(res.layers):
+        a = rows_of(L["k_codes"]).reshape(n8, Hkv, 4, 4, 4, 4, 4, 16)
+        kc[i * n8:(i + 1) * n8] = tile_order_to_token_major(a).reshape(n8, Hkv, 64, 256)
+        vc[i * n8:(i + 1) * n8] = rows_of(L["v_codes"])
+        kch[i * n8:(i + 1) * n8] = rows_of(L["k_chan"])
+        ktk[i * n8:(i + 1) * n8] = rows_of(L["k_tok"])
+        vch[i * n8:(i + 1) * n8] = rows_of(L["v_chan"])
+        kw[i * wp:(i + 1) * wp] = bits(L["k_pool"][torch.as_tensor(slw, device=L["k_pool"].device)])
+        vw[i * wp:(i + 1) * wp] = bits(L["v_pool"][torch.as_tensor(slw, device=L["v_pool"].device)])
+        q[i] = bits(L["q"][0])
+    t8_all = (np.arange(nl)[:, None] * n8 + np.arange(n8)[None, :]).astype(np.int32)
+    tw_all = (np.arange(nl)[:, None] * wp + np.arange(wp)[None, :]).astype(np.int32)
+    n8_all = np.full(nl, n8, np.int32)
+    nw_all = np.full(nl, int(plan.win_tokens[0]), np.int32)
+    log(f"[bench] cpu baseline: the step's {nl * Hkv} units copied to the host in {time.time() - t0:.1f}s")
     t0 = time.time()
-    o8, l8 = O.decode_int8(q, qz["k_codes"], qz["v_codes"], qz["k_chan"], qz["k_tok"], qz["v_chan"], t8, n8, 1,
-                           w.group, configs.SIGMA, mode=1)
-    ow, lw = O.decode_exact(q, d["k_pool"], d["v_pool"], tw, nw, 1, w.group, configs.SIGMA)
-    rows = units * w.group
-    O.merge(np.stack([o8.reshape(rows, 256), ow.reshape(rows, 256)]), np.stack([l8.reshape(rows), lw.reshape(rows)]))
+    o8, l8 = O.decode_int8(q, kc, vc, kch, ktk, vch, t8_all, n8_all, Hkv, G, res.sigma, mode=1)
+    ow, lw = O.decode_exact(q, kw, vw, tw_all, nw_all, Hkv, G, res.sigma)
+    rows = nl * Hkv * G
+    ro, rl = O.merge(np.stack([o8.reshape(rows, D), ow.reshape(rows, D)]), np.stack([l8.reshape(rows),
+                                                                                      lw.reshape(rows)]))
     wall = time.time() - t0
-    # one unit alone: the oracle's parallel loop then runs it on one thread
-    t1 = time.time()
-    O.decode_int8(q[:1], qz["k_codes"], qz["v_codes"], qz["k_chan"], qz["k_tok"], qz["v_chan"], t8[:1], n8[:1], 1,
-                  w.group, configs.SIGMA, mode=1)
-    O.decode_exact(q[:1], d["k_pool"], d["v_pool"], tw[:1], nw[:1], 1, w.group, configs.SIGMA)
-    unit_1t = time.time() - t1
-    per_step_units = w.batch * w.layers * w.num_kv_heads
-    us_per_step = wall * 1e6 * per_step_units / units
-    threads = min(O.num_threads(), units)
+    threads = min(O.num_threads(), nl * Hkv)
     cpu = "unknown CPU"
     try:
         for line in open("/proc/cpuinfo"):
@@ -580,13 +814,23 @@ def cpu_baseline(w):
                 break
     except OSError:
         pass
-    return dict(value=us_per_step, unit="us/decode step", cores=threads, kind="oracle",
-                sample=f"{units} (request, KV head) units of one {w.name} layer "
-                       f"({plan.n8[0]} int8 pages + {plan.win_tokens[0]}-token window each), "
-                       f"float64, {wall:.1f}s wall on {threads} threads of {cpu}, "
-                       f"scaled x{per_step_units / units:g} to one 16-layer step",
-                wall_s=wall, single_thread_unit_ms=unit_1t * 1e3,
-                single_thread_layer_ms=unit_1t * 1e3 * w.batch * w.num_kv_heads)
+    # the oracle check of the timed step's outputs
+    go = np.concatenate([o.reshape(-1, D).cpu().numpy() for o, _ in hyb_out]).astype(np.float64)
+    gl = np.concatenate([l.reshape(-1).cpu().numpy() for _, l in hyb_out]).astype(np.float64)
+    err = float(np.abs(go - ro).max())
+    rel = float(np.linalg.norm(go - ro) / np.linalg.norm(ro))
+    lerr = float(np.abs(gl - rl).max())
+    check = dict(layers_checked=nl, rows=rows, o_max_abs=err, o_rel_l2=rel, lse_max_abs=lerr,
+                 tolerances=dict(o_max_abs=2e-3, o_rel_l2=1e-3, lse_max_abs=1e-4),
+                 passed=bool(err <= 2e-3 and rel <= 1e-3 and lerr <= 1e-4),
+                 reference="float64 oracle (int8-path formula on the GPU's codes and scales, exact window, "
+                           "LSE merge) on the same inputs the timed step read")
+    cb = dict(value=wall * 1e6, unit="us/decode step", cores=threads, kind="oracle",
+              sample=f"all {nl * Hkv} (layer, KV head) units of one {w.name} decode step, each reading its own "
+                     f"layer's {n8} int8 pages and {plan.win_tokens[0]}-token BF16 window (the timed step's own "
+                     f"inputs, copied to the host), float64, {wall:.1f}s wall on {threads} threads of {cpu}; "
+                     f"no scaling", wall_s=wall)
+    return cb, check
 
 
 def profile_kernels(args, w):
@@ -651,6 +895,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="ctx128k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="ctx128k only: skip the 32K, batched and host-staged measurements")
     ap.add_argument("--profile-kernels", action="store_true",
                     help="for counter runs: a 1 GiB device copy (calibration), then --steps hybrid steps; no JSON")
     args = ap.parse_args()
@@ -659,20 +905,24 @@ def main():
               "head, request or page range needs no new kernel and is not run here). Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
+    import torch
+
     from quantized_paged_kv_akv_amd import configs
     w = configs.ALL[args.workload]() if args.workload in configs.ALL else configs.staged128k()
     if args.profile_kernels:
         profile_kernels(args, w)
         return
     if args.workload == "staged-sweep":
-        curve = pcie_curve()
-        rows = staged_sweep(args)
+        sw = staged_sweep(args, with_l13=True)
         print(json.dumps({"metric": "host-staged ms/token vs context, exact vs lossless 13-bit vs hybrid "
                                     "(the tier gate)",
                           "unit": "ms/token", "n_gpus": 1, "higher_is_better": False,
                           "data": "synthetic (the ctx128k recipe at each context length, pinned host history)",
-                          "pcie_h2d_curve_MiB_GBps": [[m, round(g, 2)] for m, g in curve],
-                          "contexts": rows}), flush=True)
+                          "pcie_h2d_curve_MiB_GBps": [[m, round(g, 2)] for m, g in sw["curve"]],
+                          "staged_copy_curve_MiB_GBps": {f"slots{ns}": [[m, round(g, 2)] for m, g in c]
+                                                         for ns, c in sw["staged_curve"].items()},
+                          "copy_model": staging_model_json(sw["model"]),
+                          "contexts": sw["rows"]}), flush=True)
         return
     if w.name == "staged128k":
         r = run_staged(args, w)
@@ -699,10 +949,20 @@ def main():
                       "lossless13_speedup_vs_bf16_staged": round(r["ms_b"] / r["ms_l"], 3)},
         }), flush=True)
         return
-    r = run_gpu(args, w)
+    device = torch.device("cuda", 0)
+    torch.cuda.set_device(device)
+    log(f"[bench] building {w.name}: {w.layers} layers, lengths {w.lengths[:4]}...")
+    res = Resident(w, device)
+    r = run_gpu(args, w, res)
+    cb = check = None
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (float64 oracle on the timed step's inputs) and oracle check")
+        cb, check = cpu_baseline(w, res, r["hyb_out"])
+    res.free()
+    del r["hyb_out"]
     ms = r["ms_hybrid"]
     value = r["hybrid_bytes"] / (ms * 1e-3) / 1e9
-    res = {
+    out = {
         "metric": "\u00b5s/decode step + KV bytes/s (% of HBM peak) at 128K, int8 hybrid vs BF16",
         "value": round(value, 2),
         "unit": "GB/s",
@@ -723,9 +983,12 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(r["hyb_achieved_gbps"], 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(r["hyb_achieved_gbps"] / HBM_PEAK_GBPS, 4),
                      "traffic": load_traffic("decode_hybrid_kernel", w.name),
-                     "kernel": "decode_hybrid_kernel (int8 pages + BF16 window of one layer)",
+                     "kernel": "decode_hybrid_kernel (int8 pages + BF16 window of one layer), split-K pass alone",
                      "bytes_per_launch": r["hyb_bytes_per_launch"],
-                     "avg_launch_us": round(r["hyb_launch_us"], 3)},
+                     "avg_launch_us": round(r["hyb_launch_us"], 3),
+                     "frac_step": round(value / HBM_PEAK_GBPS, 4),
+                     "frac_step_is": "whole 16-layer step (split-K kernels, second passes and launch gaps) "
+                                     "against the same peak"},
         "extra": {
             "us_per_step_hybrid": round(ms * 1e3, 2),
             "us_per_layer_hybrid": round(ms * 1e3 / w.layers, 2),
@@ -759,13 +1022,41 @@ def main():
             },
         },
     }
-    if r["owners"]:
-        res["extra"]["us_per_step_two_owner_launches"] = round(r["owners"]["ms_pairs"] * 1e3, 2)
-        res["extra"]["us_per_step_one_row_launches"] = round(r["owners"]["ms_single"] * 1e3, 2)
-    if not args.no_cpu_baseline:
-        cb = cpu_baseline(w)
-        res["cpu_baseline"] = {k: (round(v, 1) if isinstance(v, float) else v) for k, v in cb.items()}
-    print(json.dumps(res), flush=True)
+    if check is not None:
+        out["extra"]["oracle_check"] = check
+    if w.name == "ctx128k" and not args.headline_only:
+        log("[bench] ctx32k")
+        out["extra"]["ctx32k"] = run_config(args, configs.ctx32k())
+        log("[bench] batched")
+        out["extra"]["batched"] = run_config(args, configs.batched(), owner_modes=True)
+        log("[bench] host-staged sweep 8K..128K with the tier gate's transfer model")
+        sw = staged_sweep(args)
+        last = sw["last"]
+        out["extra"]["staged128k"] = {
+            "ms_per_token_hybrid": round(last["ms_h"], 3), "ms_per_token_bf16": round(last["ms_b"], 3),
+            "pcie_GBps_hybrid": round(last["bytes_h"] / (last["ms_h"] * 1e-3) / 1e9, 1),
+            "pcie_GBps_bf16": round(last["bytes_b"] / (last["ms_b"] * 1e-3) / 1e9, 1),
+            "h2d_copy_GBps": round(last["h2d_gbps"], 1), "ring_slots": RING_SLOTS[0],
+            "hybrid_frac_of_h2d_copy": round(last["bytes_h"] / (last["ms_h"] * 1e-3) / 1e9 / last["h2d_gbps"], 4),
+            "bytes_per_token_hybrid": last["bytes_h"], "bytes_per_token_bf16": last["bytes_b"],
+            "bytes_not_moved_per_token": last["bytes_b"] - last["bytes_h"],
+            "speedup_vs_bf16_staged": round(last["ms_b"] / last["ms_h"], 3)}
+        out["extra"]["tier_gate"] = {
+            "pcie_h2d_curve_MiB_GBps": [[m, round(g, 2)] for m, g in sw["curve"]],
+            "staged_copy_curve_MiB_GBps": {f"slots{ns}": [[m, round(g, 2)] for m, g in c]
+                                           for ns, c in sw["staged_curve"].items()},
+            "copy_model": staging_model_json(sw["model"]),
+            "ring_slots_measured": list(RING_SLOTS),
+            "contexts": sw["rows"],
+            "max_abs_prediction_error": round(max(max(abs(x[f"slots{k}"]["prediction_error_hybrid"]),
+                                                      abs(x[f"slots{k}"]["prediction_error_bf16"]))
+                                                  for x in sw["rows"] for k in RING_SLOTS), 4),
+            "model_choice_equals_measured_argmin": all(x[f"slots{k}"]["chosen_by_model"] ==
+                                                       x[f"slots{k}"]["chosen_by_measurement"]
+                                                       for x in sw["rows"] for k in RING_SLOTS)}
+    if cb is not None:
+        out["cpu_baseline"] = {k: (round(v, 1) if isinstance(v, float) else v) for k, v in cb.items()}
+    print(json.dumps(out), flush=True)
 
 
 if __name__ == "__main__":

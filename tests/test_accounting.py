@@ -55,3 +55,18 @@ def test_ctx32k_step_bytes():
     assert plan.n8 == [496] and plan.win_tokens == [1024]
     b = bench.step_kv_bytes(plan, w.num_kv_heads)
     assert w.layers * (b["int8"] + b["window"]) == 1_180_434_432
+
+
+def test_tile_order_transpose_matches_the_header_formula():
+    """The benchmark's transpose of tile-ordered key codes back to token-major
+    order equals indexing by the byte offsets include/akv.h states."""
+    import numpy as np
+
+    t = np.arange(64)[:, None]
+    d = np.arange(256)[None, :]
+    off = ((4 * (d // 64) + (t // 4) % 4) * 64 + 16 * ((d // 16) % 4) + 4 * (t // 16) + t % 4) * 16 + d % 16
+    assert sorted(off.reshape(-1).tolist()) == list(range(16384))
+    tiled = np.random.default_rng(0).integers(-127, 128, size=(3, 2, 16384)).astype(np.int8)
+    ref = tiled[..., off.reshape(-1)].reshape(3, 2, 64, 256)
+    got = bench.tile_order_to_token_major(tiled.reshape(3, 2, 4, 4, 4, 4, 4, 16)).reshape(3, 2, 64, 256)
+    assert np.array_equal(got, ref)
