@@ -825,11 +825,13 @@ def cpu_baseline(w, res, hyb_out):
                  passed=bool(err <= 2e-3 and rel <= 1e-3 and lerr <= 1e-4),
                  reference="float64 oracle (int8-path formula on the GPU's codes and scales, exact window, "
                            "LSE merge) on the same inputs the timed step read")
-    cb = dict(value=wall * 1e6, unit="us/decode step", cores=threads, kind="oracle",
+    step_bytes = res.layer_bytes * nl
+    cb = dict(value=round(step_bytes / wall / 1e9, 3), unit="GB/s", cores=threads, kind="oracle",
               sample=f"all {nl * Hkv} (layer, KV head) units of one {w.name} decode step, each reading its own "
                      f"layer's {n8} int8 pages and {plan.win_tokens[0]}-token BF16 window (the timed step's own "
                      f"inputs, copied to the host), float64, {wall:.1f}s wall on {threads} threads of {cpu}; "
-                     f"no scaling", wall_s=wall)
+                     f"value = the step's {step_bytes} algorithmic KV bytes / that wall time",
+              us_per_step=round(wall * 1e6, 1), wall_s=wall)
     return cb, check
 
 
