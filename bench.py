@@ -109,14 +109,20 @@ def build_layers(w, device):
     return plan, layers, tables, qt_ms, len(src)
 
 
-def timed_steps(fn, steps, warmup, stream):
-    """Average ms of `steps` calls of fn after `warmup` untimed ones, bracketed
+def timed_steps(fn, steps, warmup, stream, min_warm_s=0.3):
+    """Average ms of `steps` calls of fn after `warmup` untimed ones (and more
+    untimed calls until they have run for min_warm_s: the first ~20 steps
+    after the GPU idles run up to 2% slow while its clocks ramp), bracketed
     by device synchronisation and HIP events on `stream`."""
     import torch
 
+    t0 = time.time()
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    while time.time() - t0 < min_warm_s:
+        fn()
+        torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(steps):
@@ -901,6 +907,8 @@ def main():
                     help="ctx128k only: skip the 32K, batched and host-staged measurements")
     ap.add_argument("--profile-kernels", action="store_true",
                     help="for counter runs: a 1 GiB device copy (calibration), then --steps hybrid steps; no JSON")
+    ap.add_argument("--pv-fp16", action="store_true",
+                    help="A/B: the int8 tier's PV product on FP16 operands instead of the int8 MFMA")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only (one GPU's share of the path at its real shape; sharding by KV "
@@ -909,7 +917,10 @@ def main():
 
     import torch
 
+    from quantized_paged_kv_akv_amd import binding as B
     from quantized_paged_kv_akv_amd import configs
+    if args.pv_fp16:
+        B.akv_set_launch_shape(pv_fp16=1)
     w = configs.ALL[args.workload]() if args.workload in configs.ALL else configs.staged128k()
     if args.profile_kernels:
         profile_kernels(args, w)
@@ -981,7 +992,8 @@ def main():
         "config": {"workload": w.name, "context_tokens": int(w.lengths[0]), "batch": w.batch,
                    "layers": w.layers, "kv_heads": w.num_kv_heads, "group": w.group, "head_dim": w.head_dim,
                    "page": w.page, "bf16_window_tokens": w.window, "parallelism": "single GPU",
-                   "launch": "eager; per layer akv_decode_hybrid = split-K kernel + combine kernel"},
+                   "launch": "eager; per layer akv_decode_hybrid = split-K kernel + combine kernel",
+                   "pv_operand": "fp16 hi+lo" if args.pv_fp16 else "int8 MFMA, 3 fixed-point limbs"},
         "roofline": {"bound": "hbm", "achieved": round(r["hyb_achieved_gbps"], 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(r["hyb_achieved_gbps"] / HBM_PEAK_GBPS, 4),
                      "traffic": load_traffic("decode_hybrid_kernel", w.name),

@@ -114,18 +114,29 @@ akv_status akv_set_profile_events(void *start_event, void *stop_event);
  *                        four waves), at most 64;
  *   hybrid_int8_pages    akv_decode_hybrid: int8 pages per work-group, at
  *                        most 256;
- *   hybrid_window_pages  akv_decode_hybrid: window pages per work-group.
+ *   hybrid_window_pages  akv_decode_hybrid: window pages per work-group;
+ *   pv_fp16              akv_decode_attn_int8 / akv_decode_hybrid: 1 runs the
+ *                        int8 tier's PV product on FP16 operands (the softmax
+ *                        weights as FP16 hi + lo against value codes turned
+ *                        into FP16) instead of the int8 MFMA (the weights as
+ *                        three 7-bit fixed-point limbs against the raw codes);
+ *                        for A/B measurement ("SYCL" page, "Attention that
+ *                        reads 8-bit history": which products run on integers
+ *                        is decided by measurement).  Both stay within the
+ *                        acceptance tolerances.
  * NULL restores the plan.  The workspace size queries follow the same
  * setting, so change it only between a query and the calls it sized.
- * Results do not depend on the shape beyond FP32 rounding order.
- * Errors: AKV_ERR_ARG for a negative field or one beyond its limit (nothing
- * is changed then).
+ * Results do not depend on the shape beyond FP32 rounding order (and, for
+ * pv_fp16, the weights' rounding: 22 significant bits either way).
+ * Errors: AKV_ERR_ARG for a negative field, one beyond its limit or pv_fp16
+ * other than 0 or 1 (nothing is changed then).
  */
 typedef struct {
     int32_t pages_per_split;
     int32_t pages_per_wave;
     int32_t hybrid_int8_pages;
     int32_t hybrid_window_pages;
+    int32_t pv_fp16;
 } akv_launch_shape;
 akv_status akv_set_launch_shape(const akv_launch_shape *shape);
 

@@ -21,6 +21,8 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 // the events bracket that kernel's dispatch and execution.
 hipEvent_t prof_start_event();
 hipEvent_t prof_stop_event();
+// the calling thread's launch shape asks for the FP16 PV operand of the int8 tier
+bool pv_fp16();
 
 // Shape checks common to every attention/quantize call.
 akv_status check_dims(const akv_dims* d);

@@ -205,6 +205,18 @@ struct Int8Smem {
     float ml[4][kMaxGroup];        // ... its sum of weights
 };
 
+// The PV operand of the int8 tier comes in two forms ("SYCL" page, "Attention
+// that reads 8-bit history": which products run on integers was decided by
+// measurement):
+//   kPvI8   the weights P <= 1 as Y = rint(P (2^21 - 1)), split into three
+//           7-bit limbs (Y = 2^14 l0 + 2^7 l1 + l2), against the raw value
+//           codes on the int8 MFMA: exact int32 sums, no code conversion;
+//   kPvF16  P as FP16 hi + lo against the value codes turned into FP16.
+// The int8 form is the default; the FP16 form stays selectable for A/B runs.
+constexpr int kPvF16 = 0;
+constexpr int kPvI8 = 3;
+
+template <int PvLimbs>
 __device__ __forceinline__ void int8_split(const Int8Args& a, Int8Smem& sm, int split, int kvh, int b) {
     const int np = min(a.n_pages[b], a.max_pages);
     // this work-group's pages [wg0, wg0 + len): a near-equal share of the request's
@@ -222,6 +234,13 @@ __device__ __forceinline__ void int8_split(const Int8Args& a, Int8Smem& sm, int 
     const int hh = n >> 1;
     const bool lo_lane = (n & 1) != 0;
     const float lo_m = lo_lane ? 1.0f : 0.0f;
+    // int8 PV limbs: limb 0 in even columns and limb 1 in odd columns of the
+    // first operand, limb 2 in odd columns of the second (its even columns are
+    // zero); an even lane accumulates 128 l0-sums, an odd lane 128 l1-sums +
+    // l2-sums, and the end merge weighs the pair 128 : 1 over 2^21 - 1
+    constexpr float pv_scale = 2097151.0f;
+    const uint32_t pv_shift = lo_lane ? 7u : 14u;
+    const uint32_t pv_mask_b = lo_lane ? 0x7Fu : 0u;
     // wave w reads the work-group's pages w, w + 4, w + 8, ...: at any moment
     // the four waves stream neighbouring pages, which the memory system serves
     // better than four distant ranges.  The loop runs p = pa .. pb - 1 over
@@ -358,14 +377,33 @@ __device__ __forceinline__ void int8_split(const Int8Args& a, Int8Smem& sm, int 
             // every column's rescale factor is exactly 1 on most pages: skip it
             const bool rescale = __builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0;
             half8 pbo[2];
+            u32x4 pla = {0, 0, 0, 0}, plb = {0, 0, 0, 0};
+            if constexpr (PvLimbs == kPvF16) {
 #pragma unroll
-            for (int s = 0; s < 2; ++s)
+                for (int s = 0; s < 2; ++s)
 #pragma unroll
-                for (int e = 0; e < 8; e += 2) {
-                    const half2 v = split_sel_f16x2(p_elem(pr, s, e), p_elem(pr, s, e + 1), lo_m);
-                    pbo[s][e] = v[0];
-                    pbo[s][e + 1] = v[1];
+                    for (int e = 0; e < 8; e += 2) {
+                        const half2 v = split_sel_f16x2(p_elem(pr, s, e), p_elem(pr, s, e + 1), lo_m);
+                        pbo[s][e] = v[0];
+                        pbo[s][e + 1] = v[1];
+                    }
+            } else {
+                // Y = rint(p (2^21 - 1)), read from the mantissa of p S + 2^23
+                // (p <= 1, so the sum stays in [2^23, 2^24) where the ulp is 1).
+                // Operand byte i is token 16g + i, the order of the value row.
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    uint32_t wa = 0, wb = 0;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t y = __builtin_bit_cast(uint32_t, __builtin_fmaf(pr[4 * k + e], pv_scale, 8388608.0f));
+                        wa |= __builtin_amdgcn_ubfe(y, pv_shift, 7) << (8 * e);
+                        wb |= (y & pv_mask_b) << (8 * e);
+                    }
+                    pla[k] = wa;
+                    plb[k] = wb;
                 }
+            }
             if (rescale) {
 #pragma unroll
                 for (int j = 0; j < 16; ++j) O[j] = O[j] * alpha;
@@ -374,11 +412,20 @@ __device__ __forceinline__ void int8_split(const Int8Args& a, Int8Smem& sm, int 
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
                 const u32x4 vv = buf[j];
-                const half8 a0 = i8x8_to_f16(vv.x, vv.y);
-                const half8 a1 = i8x8_to_f16(vv.z, vv.w);
                 f32x4 c = {0.0f, 0.0f, 0.0f, 0.0f};
-                c = mfma_f16(a0, pbo[0], c);
-                c = mfma_f16(a1, pbo[1], c);
+                if constexpr (PvLimbs == kPvF16) {
+                    const half8 a0 = i8x8_to_f16(vv.x, vv.y);
+                    const half8 a1 = i8x8_to_f16(vv.z, vv.w);
+                    c = mfma_f16(a0, pbo[0], c);
+                    c = mfma_f16(a1, pbo[1], c);
+                } else {
+                    // 128 ca + cb stays below 2^31 (|ca| <= 64 * 127 * 127)
+                    const i32x4 z4 = {0, 0, 0, 0};
+                    const i32x4 ca = mfma_i8(vv, pla, z4);
+                    const i32x4 cb = mfma_i8(vv, plb, z4);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) c[r] = (float)(ca[r] * 128 + cb[r]);
+                }
                 const f32x4 vs = *reinterpret_cast<const f32x4*>(&scl[kD + 16 * j + 4 * g]);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) O[j][r] = O[j][r] + vs[r] * c[r];
@@ -398,10 +445,13 @@ __device__ __forceinline__ void int8_split(const Int8Args& a, Int8Smem& sm, int 
 
     // merge the four waves: each publishes its unnormalised O, max and weight sum
     const float L = group_sum(lsum);
+    // the column pair's parts: hi + lo, or the limb sums weighed 128 : 1 over S
+    const float w_self = PvLimbs == kPvF16 ? 1.0f : 128.0f / pv_scale;
+    const float w_pair = PvLimbs == kPvF16 ? 1.0f : 1.0f / pv_scale;
 #pragma unroll
     for (int j = 0; j < 16; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) O[j][r] += swap_pair(O[j][r]);
+        for (int r = 0; r < 4; ++r) O[j][r] = O[j][r] * w_self + swap_pair(O[j][r]) * w_pair;
     if (!lo_lane) {
 #pragma unroll
         for (int j = 0; j < 16; ++j)
@@ -704,9 +754,10 @@ union SplitSmem {
     } bx;
 };
 
+template <int PvLimbs>
 __global__ __launch_bounds__(kThreads, 2) void decode_int8_kernel(Int8Args a) {
     __shared__ Int8Smem sm;
-    int8_split(a, sm, blockIdx.x, blockIdx.y, blockIdx.z);
+    int8_split<PvLimbs>(a, sm, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 __global__ __launch_bounds__(kThreads, 2) void decode_exact_kernel(ExactArgs a) {
@@ -727,12 +778,13 @@ __global__ __launch_bounds__(kThreads, 2) void decode_l13_kernel(ExactArgs a, L1
 // read the BF16 window (dispatched first: they are the short ones), the rest
 // read int8 pages; all write partial columns of the same rows (int8 columns
 // first, window columns after them).
+template <int PvLimbs>
 __global__ __launch_bounds__(kThreads, 2) void decode_hybrid_kernel(Int8Args a8, ExactArgs ax, int nw) {
     __shared__ SplitSmem sm;
     if ((int)blockIdx.x < nw)
         exact_split(ax, Bf16Source{ax.kb, ax.vb, sm.bx.st.q[threadIdx.x >> 6]}, sm.bx.ex, blockIdx.x, blockIdx.y, blockIdx.z);
     else
-        int8_split(a8, sm.i8, blockIdx.x - nw, blockIdx.y, blockIdx.z);
+        int8_split<PvLimbs>(a8, sm.i8, blockIdx.x - nw, blockIdx.y, blockIdx.z);
 }
 
 // Tensors: non-NULL and 16-byte aligned.  int32 page tables and length
@@ -891,7 +943,10 @@ extern "C" akv_status akv_decode_attn_int8(const akv_dims* dims, int32_t batch, 
                            softmax_scale, plan);
     split_workspace(dims, batch, plan.n_splits, workspace, &a.part_o, &a.part_lse);
     dim3 grid((unsigned)plan.n_splits, (unsigned)dims->num_kv_heads, (unsigned)batch);
-    launch_split(decode_int8_kernel, grid, s, a);
+    if (pv_fp16())
+        launch_split(decode_int8_kernel<kPvF16>, grid, s, a);
+    else
+        launch_split(decode_int8_kernel<kPvI8>, grid, s, a);
     if ((st = launch_status("decode_int8_kernel")) != AKV_OK) return st;
     return launch_combine(rows, dims->head_dim, a.part_o, a.part_lse, plan.n_splits, out_o, out_lse, s);
 }
@@ -979,7 +1034,10 @@ static akv_status decode_hybrid_impl(const akv_dims* dims, int32_t batch, const 
     ax.part_o = a8.part_o;
     ax.part_lse = a8.part_lse;
     dim3 grid((unsigned)n_cols, (unsigned)dims->num_kv_heads, (unsigned)batch);
-    launch_split(decode_hybrid_kernel, grid, s, a8, ax, pw.n_splits);
+    if (pv_fp16())
+        launch_split(decode_hybrid_kernel<kPvF16>, grid, s, a8, ax, pw.n_splits);
+    else
+        launch_split(decode_hybrid_kernel<kPvI8>, grid, s, a8, ax, pw.n_splits);
     if ((st = launch_status("decode_hybrid_kernel")) != AKV_OK) return st;
     return launch_combine(rows, dims->head_dim, a8.part_o, a8.part_lse, n_cols, out_o, out_lse, s);
 }

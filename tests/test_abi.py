@@ -127,7 +127,7 @@ def test_launch_shape_validation(B):
     d = B.dims(4, 6)
     planned = B.akv_decode_workspace_bytes(d, 1, 2032)
     for bad in (dict(pages_per_split=-1), dict(pages_per_wave=65), dict(hybrid_int8_pages=257),
-                dict(hybrid_window_pages=-3)):
+                dict(hybrid_window_pages=-3), dict(pv_fp16=2), dict(pv_fp16=-1)):
         with pytest.raises(B.AkvError) as e:
             B.akv_set_launch_shape(**bad)
         assert e.value.status_name == "AKV_ERR_ARG"
@@ -139,6 +139,9 @@ def test_launch_shape_validation(B):
         B.akv_set_launch_shape(hybrid_int8_pages=8, hybrid_window_pages=1)
         need = B.akv_decode_hybrid_workspace_bytes(d, 1, 2032, 16)
         assert need >= 24 * (254 + 16) * 257 * 4
+        # the PV operand choice does not change the plan
+        B.akv_set_launch_shape(pv_fp16=1)
+        assert B.akv_decode_workspace_bytes(d, 1, 2032) == planned
     finally:
         B.akv_set_launch_shape(reset=True)
     assert B.akv_decode_workspace_bytes(d, 1, 2032) == planned

@@ -177,6 +177,25 @@ def test_int8_long_context(B, pages_per_wave):
     check_attn(o, lse, ro, rl, "int8 8192 pages")
 
 
+@pytest.mark.parametrize("pv_fp16", [0, 1])
+def test_int8_pv_operands_agree(B, pv_fp16):
+    """The int8 tier's PV product on the int8 MFMA (weights as three 7-bit
+    fixed-point limbs, the default) and on FP16 operands (weights hi + lo,
+    codes turned into FP16): each within the tolerances of the oracle, and
+    the two within 1e-4 of each other."""
+    say(f"case int8 PV operand, pv_fp16={pv_fp16}")
+    g, table, q = _int8_case(B, 515, 4, 6, [300, 41])
+    B.akv_set_launch_shape(pv_fp16=pv_fp16)
+    try:
+        o, lse = run_int8(B, 4, 6, q, g, table, [300, 41])
+    finally:
+        B.akv_set_launch_shape(reset=True)
+    ro, rl = oracle_int8(O, 4, 6, q, g, table, [300, 41])
+    check_attn(o, lse, ro, rl, f"int8 PV operand fp16={pv_fp16}")
+    o_other, l_other = run_int8(B, 4, 6, q, g, table, [300, 41]) if pv_fp16 else (o, lse)
+    assert float((o - o_other).abs().max()) <= 1e-4 and float((lse - l_other).abs().max()) <= 1e-5
+
+
 def test_int8_decode_deterministic(B):
     g, table, q = _int8_case(B, 7, 4, 6, [150])
     say("case int8 determinism")
