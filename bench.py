@@ -844,7 +844,8 @@ def cpu_baseline(w, res, hyb_out):
 def profile_kernels(args, w):
     """Kernel sequence for rocprofv3 counter passes: a plain 1 GiB device copy
     (known bytes, to calibrate FETCH_SIZE / WRITE_SIZE), then `steps` hybrid
-    decode steps of the workload."""
+    decode steps of the workload, then `steps` steps of the int8 tier alone
+    (akv_decode_attn_int8: one wave per int8 page-head, for per-page counts)."""
     import torch
 
     from quantized_paged_kv_akv_amd import binding as B
@@ -873,6 +874,14 @@ def profile_kernels(args, w):
                                 configs.SIGMA, o, lse, ws)
     torch.cuda.synchronize()
     log(f"[profile] {args.steps} hybrid steps done")
+    # the int8 tier alone (one wave per page-head): per-page instruction counts
+    ws8 = torch.empty(max(16, B.akv_decode_workspace_bytes(dims, w.batch, m8)), dtype=torch.uint8, device=device)
+    for _ in range(args.steps):
+        for L in layers:
+            B.akv_decode_attn_int8(dims, w.batch, L["q"], L["k_codes"], L["v_codes"], L["k_chan"], L["k_tok"],
+                                   L["v_chan"], T["t8"], T["n8"], m8, configs.SIGMA, o, lse, ws8)
+    torch.cuda.synchronize()
+    log(f"[profile] {args.steps} int8-only steps done")
 
 
 def load_traffic(kernel: str, workload: str):
