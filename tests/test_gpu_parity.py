@@ -196,6 +196,25 @@ def test_int8_pv_operands_agree(B, pv_fp16):
     assert float((o - o_other).abs().max()) <= 1e-4 and float((lse - l_other).abs().max()) <= 1e-5
 
 
+@pytest.mark.parametrize("weights", ["uniform", "sharp"])
+def test_int8_pv_limbs_degenerate_weights(B, weights):
+    """The softmax weights' fixed-point limbs at their ends: q = 0 makes every
+    weight exactly 1 (every limb 127; O is the mean of the dequantized values,
+    LSE = ln(tokens)), and a query 4x the usual scale makes the attention so
+    sharp that most weights round to 0 against the largest."""
+    say(f"case int8 PV limbs, {weights} weights")
+    g, table, q = _int8_case(B, 616, 2, 6, [90, 7])
+    if weights == "uniform":
+        q = np.zeros_like(q)
+    else:
+        q = inputs.random_queries(617, 2, 12, scale=4.0)
+    o, lse = run_int8(B, 2, 6, q, g, table, [90, 7])
+    ro, rl = oracle_int8(O, 2, 6, q, g, table, [90, 7])
+    check_attn(o, lse, ro, rl, f"int8 PV limbs {weights}")
+    if weights == "uniform":
+        assert np.allclose(host(lse), np.log(np.array([90, 7]) * 64.0)[:, None], atol=1e-5)
+
+
 def test_int8_decode_deterministic(B):
     g, table, q = _int8_case(B, 7, 4, 6, [150])
     say("case int8 determinism")
