@@ -12,15 +12,18 @@
 // tier first"), expanding each operand register to BF16 right before its
 // MFMA, so its results are bit-identical to the BF16 pages'.
 //
-// Both tiers contract with 16x16x32 MFMAs (FP16 for int8 codes, which become
-// FP16 exactly; BF16 for the exact tier), QK as S^T (tokens x heads) = K Q^T
-// and PV as O^T (channels x heads) = V^T P^T, with V stored channel-major so
-// 16 bytes of a value row are one PV operand (int8 tiles are loaded straight
-// into operand registers; BF16 pages are loaded in whole lines and their
-// operands rebuilt through LDS, see Bf16Source).  The 16 MFMA columns carry each
-// query head twice, so an FP32 operand (q' for the int8 tier, the softmax
-// weights P for both) is fed as a high and a low half-precision part in one
-// MFMA and the two halves of the result are added afterwards.
+// QK is S^T (tokens x heads) = K Q^T and PV is O^T (channels x heads) =
+// V^T P^T, with V stored channel-major so 16 bytes of a value row are one PV
+// operand (int8 tiles are loaded straight into operand registers; BF16 pages
+// are loaded in whole lines and their operands rebuilt through LDS, see
+// Bf16Source).  The exact tier contracts both on 16x16x32 BF16 MFMAs.  The
+// int8 tier runs QK on 16x16x32 FP16 MFMAs (int8 codes become FP16 exactly)
+// and PV on 16x16x64 int8 MFMAs against the raw value codes.  The 16 MFMA
+// columns carry each query head twice: an FP32 operand (q' for the int8 tier,
+// the softmax weights P for the exact tier) is fed as a high and a low
+// half-precision part in one MFMA and the two halves of the result are added
+// afterwards; the int8 tier's weights go in as fixed-point limbs (see
+// kPvI8), two in one operand's column pair and a third in a second operand.
 //
 // Work decomposition.  int8 tier: one wave owns whole pages (no barrier per
 // page); a work-group's four waves share a range of one (request, KV head)'s
@@ -185,8 +188,9 @@ __device__ __forceinline__ void write_empty(int G, int Hkv, int kvh, int b, int 
 //        32 MFMAs.
 //   softmax over the lane's 16 logits (tokens 16g .. 16g+15) and the group.
 //   PV   channel tile j: the lane's 16-byte load V^T[16j + n][16g .. +16] is
-//        the A operand of two k-steps, P^T the B operand (hi part of head n>>1
-//        in even columns, lo part in odd ones).  32 MFMAs.
+//        the A operand of one int8 k-step over the page's 64 tokens, P^T the
+//        B operand as limbs of head n>>1 (two int8 MFMAs: limbs 0 and 1, then
+//        limb 2).  32 MFMAs.
 // Code tiles stream with the non-temporal hint (each is read once, in whole
 // lines).  The query's FP32 rows sit in LDS; each query row is pre-scaled by a power
 // of two so max|q| < 1, which with max_d c_d >= 1 (the factors multiply to
