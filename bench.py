@@ -571,11 +571,16 @@ def run_staged(args, w, with_l13=True, ring_slots=(2,)):
         enq[name] = (time.perf_counter() - t_h) * 1e3
         torch.cuda.synchronize()
     steps = max(2, args.steps // 4)
+
+    def best_of_two(fn):
+        # the faster of two timed runs (a single run can catch other traffic on the bus)
+        return min(timed_steps(fn, steps, 1, comp), timed_steps(fn, steps, 0, comp, min_warm_s=0.0))
+
     by_slots = {}
     for k in ring_slots:
         cur["h"], cur["b"] = rings_h[k], rings_b[k]
         log(f"[bench] {w.name}: staged hybrid and all-BF16 steps, {k}-slot ring")
-        by_slots[k] = dict(ms_h=timed_steps(hybrid_step, steps, 1, comp), ms_b=timed_steps(bf16_step, steps, 1, comp))
+        by_slots[k] = dict(ms_h=best_of_two(hybrid_step), ms_b=best_of_two(bf16_step))
     ms_h, ms_b = by_slots[ring_slots[0]]["ms_h"], by_slots[ring_slots[0]]["ms_b"]
     for k in ring_slots:
         if k != n_ring:
@@ -584,7 +589,7 @@ def run_staged(args, w, with_l13=True, ring_slots=(2,)):
     ms_l = None
     if with_l13:
         log(f"[bench] {w.name}: staged lossless 13-bit step")
-        ms_l = timed_steps(l13_step, steps, 1, comp)
+        ms_l = best_of_two(l13_step)
         ring_l.destroy()
     ring_h.destroy()
     ring_b.destroy()
@@ -613,13 +618,16 @@ def pcie_curve(sizes_mib=(0.0625, 0.25, 1, 4, 16, 64, 256, 512)):
         reps = max(3, min(200, int(256 / max(mib, 1e-3))))
         dst[:n].copy_(big[:n], non_blocking=True)
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            dst[:n].copy_(big[:n], non_blocking=True)
-        e1.record()
-        torch.cuda.synchronize()
-        out.append((mib, reps * n / (e0.elapsed_time(e1) * 1e-3) / 1e9))
+        best = float("inf")
+        for _ in range(3):  # the fastest of three runs
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                dst[:n].copy_(big[:n], non_blocking=True)
+            e1.record()
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1))
+        out.append((mib, reps * n / (best * 1e-3) / 1e9))
     return out
 
 
@@ -654,12 +662,15 @@ def staged_copy_curve(sizes_mib=(1, 4, 8, 16, 32, 64, 128, 256), n_slots=2):
         while time.time() - t_warm < 0.2:
             run(8)
             torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(comp)
-        run(reps)
-        e1.record(comp)
-        torch.cuda.synchronize()
-        out.append((mib, reps * n / (e0.elapsed_time(e1) * 1e-3) / 1e9))
+        best = float("inf")
+        for _ in range(3):  # the fastest of three runs: single runs catch other traffic on the bus
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(comp)
+            run(reps)
+            e1.record(comp)
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1))
+        out.append((mib, reps * n / (best * 1e-3) / 1e9))
         ring.destroy()
     return out
 
