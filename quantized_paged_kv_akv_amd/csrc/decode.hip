@@ -778,17 +778,20 @@ __global__ __launch_bounds__(kThreads, 2) void decode_l13_kernel(ExactArgs a, L1
     exact_split(a, src, sm, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
-// Both tiers of a layer in one launch: the first nw work-groups of each row
-// read the BF16 window (dispatched first: they are the short ones), the rest
-// read int8 pages; all write partial columns of the same rows (int8 columns
-// first, window columns after them).
+// Both tiers of a layer in one launch: in each (request, KV head) row of the
+// grid the int8 work-groups come first and the last nw read the BF16 window
+// (measured against window-first: the same at 128K, 2 us faster per 32K step,
+// 0.8% faster batched); all write partial columns of the same rows (int8
+// columns first, window columns after them).
 template <int PvLimbs>
 __global__ __launch_bounds__(kThreads, 2) void decode_hybrid_kernel(Int8Args a8, ExactArgs ax, int nw) {
     __shared__ SplitSmem sm;
-    if ((int)blockIdx.x < nw)
-        exact_split(ax, Bf16Source{ax.kb, ax.vb, sm.bx.st.q[threadIdx.x >> 6]}, sm.bx.ex, blockIdx.x, blockIdx.y, blockIdx.z);
+    const int n8s = (int)gridDim.x - nw;
+    if ((int)blockIdx.x >= n8s)
+        exact_split(ax, Bf16Source{ax.kb, ax.vb, sm.bx.st.q[threadIdx.x >> 6]}, sm.bx.ex, blockIdx.x - n8s, blockIdx.y,
+                    blockIdx.z);
     else
-        int8_split<PvLimbs>(a8, sm.i8, blockIdx.x - nw, blockIdx.y, blockIdx.z);
+        int8_split<PvLimbs>(a8, sm.i8, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 // Tensors: non-NULL and 16-byte aligned.  int32 page tables and length
