@@ -65,20 +65,34 @@ __host__ __device__ __forceinline__ int kcode_offset(int t, int d) {
     return (tile * 64 + lane) * 16 + (d & 15);
 }
 
-// Signed int8 codes -> exact FP16.  Each byte b is biased to b + 128 (xor
-// 0x80), placed under the exponent byte 0x64 (FP16 0x64XX = 1024 + XX) with a
-// byte permute, and the packed result minus 1152 is b exactly.
+// Two signed int8 codes (bytes 2k and 2k+1 of w) -> two exact FP16 values in
+// one register: one sub-dword conversion per code, each sign-extending its
+// byte, converting it (every int8 value is an FP16 integer) and writing one
+// half of the destination, the second keeping the half the first wrote.  One
+// instruction per code, against 1.25 for a byte permute under an FP16
+// exponent byte followed by a packed bias subtraction (measured: 4 us less
+// per 16-layer 32K step, bit-identical results).
+template <int K>
+__device__ __forceinline__ uint32_t i8x2_to_f16x2(uint32_t w) {
+    static_assert(K == 0 || K == 1, "byte pair 0 or 1");
+    uint32_t r;
+    if constexpr (K == 0)
+        asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_0\n\t"
+            "v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_1"
+            : "=&v"(r)
+            : "v"(w));
+    else
+        asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_2\n\t"
+            "v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_3"
+            : "=&v"(r)
+            : "v"(w));
+    return r;
+}
+
+// Eight signed int8 codes (w0 bytes 0..3, then w1) -> exact FP16, in order.
 __device__ __forceinline__ half8 i8x8_to_f16(uint32_t w0, uint32_t w1) {
-    const uint32_t x0 = w0 ^ 0x80808080u, x1 = w1 ^ 0x80808080u;
-    // v_perm_b32: bytes 0..3 come from the second operand, 4..7 from the first
-    u32x4 r;
-    r.x = __builtin_amdgcn_perm(0x64646464u, x0, 0x04010400u);
-    r.y = __builtin_amdgcn_perm(0x64646464u, x0, 0x04030402u);
-    r.z = __builtin_amdgcn_perm(0x64646464u, x1, 0x04010400u);
-    r.w = __builtin_amdgcn_perm(0x64646464u, x1, 0x04030402u);
-    half8 h = __builtin_bit_cast(half8, r);
-    const half8 bias = {1152, 1152, 1152, 1152, 1152, 1152, 1152, 1152};
-    return h - bias;
+    const u32x4 r = {i8x2_to_f16x2<0>(w0), i8x2_to_f16x2<1>(w0), i8x2_to_f16x2<0>(w1), i8x2_to_f16x2<1>(w1)};
+    return __builtin_bit_cast(half8, r);
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
