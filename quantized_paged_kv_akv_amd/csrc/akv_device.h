@@ -65,33 +65,33 @@ __host__ __device__ __forceinline__ int kcode_offset(int t, int d) {
     return (tile * 64 + lane) * 16 + (d & 15);
 }
 
-// Two signed int8 codes (bytes 2k and 2k+1 of w) -> two exact FP16 values in
-// one register: one sub-dword conversion per code, each sign-extending its
-// byte, converting it (every int8 value is an FP16 integer) and writing one
-// half of the destination, the second keeping the half the first wrote.  One
-// instruction per code, against 1.25 for a byte permute under an FP16
-// exponent byte followed by a packed bias subtraction (measured: 4 us less
-// per 16-layer 32K step, bit-identical results).
-template <int K>
-__device__ __forceinline__ uint32_t i8x2_to_f16x2(uint32_t w) {
-    static_assert(K == 0 || K == 1, "byte pair 0 or 1");
-    uint32_t r;
-    if constexpr (K == 0)
-        asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_0\n\t"
-            "v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_1"
-            : "=&v"(r)
-            : "v"(w));
-    else
-        asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_2\n\t"
-            "v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_3"
-            : "=&v"(r)
-            : "v"(w));
-    return r;
-}
-
-// Eight signed int8 codes (w0 bytes 0..3, then w1) -> exact FP16, in order.
+// Eight signed int8 codes (w0 bytes 0..3, then w1) -> exact FP16, in order:
+// one sub-dword conversion per code that sign-extends its byte (every int8
+// value is an FP16 integer) and writes one half of a result register; one
+// instruction per code against 1.25 for a byte permute under an FP16 exponent
+// byte and a packed bias subtraction (4 us less per 16-layer 32K step,
+// bit-identical results).  On gfx950 an instruction that writes part of a
+// register must not be followed at once by one that reads that register, and
+// the compiler cannot space instructions inside an asm block: so the four low
+// halves are written first, the four high halves (which keep the low ones)
+// after them, and a closing s_nop keeps the last write one instruction away
+// from its first reader.  (Written as pairs, each high-half write right after
+// its low half, the outputs went wrong as soon as the waves' issue priorities
+// were changed.)
 __device__ __forceinline__ half8 i8x8_to_f16(uint32_t w0, uint32_t w1) {
-    const u32x4 r = {i8x2_to_f16x2<0>(w0), i8x2_to_f16x2<1>(w0), i8x2_to_f16x2<0>(w1), i8x2_to_f16x2<1>(w1)};
+    uint32_t r0, r1, r2, r3;
+    asm("v_cvt_f16_i16_sdwa %0, sext(%4) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_0\n\t"
+        "v_cvt_f16_i16_sdwa %1, sext(%4) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_2\n\t"
+        "v_cvt_f16_i16_sdwa %2, sext(%5) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_0\n\t"
+        "v_cvt_f16_i16_sdwa %3, sext(%5) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_2\n\t"
+        "v_cvt_f16_i16_sdwa %0, sext(%4) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_1\n\t"
+        "v_cvt_f16_i16_sdwa %1, sext(%4) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_3\n\t"
+        "v_cvt_f16_i16_sdwa %2, sext(%5) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_1\n\t"
+        "v_cvt_f16_i16_sdwa %3, sext(%5) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_3\n\t"
+        "s_nop 0"
+        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+        : "v"(w0), "v"(w1));
+    const u32x4 r = {r0, r1, r2, r3};
     return __builtin_bit_cast(half8, r);
 }
 
