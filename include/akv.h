@@ -123,13 +123,25 @@ akv_status akv_set_profile_events(void *start_event, void *stop_event);
  *                        for A/B measurement ("SYCL" page, "Attention that
  *                        reads 8-bit history": which products run on integers
  *                        is decided by measurement).  Both stay within the
- *                        acceptance tolerances.
+ *                        acceptance tolerances;
+ *   issue_priority       akv_decode_attn_int8 / _exact / _l13 /
+ *                        akv_decode_hybrid(_static): a scheduling probe for
+ *                        tests.  0 leaves every wave at the default issue
+ *                        priority; 1 sets each decode wave's priority
+ *                        (s_setprio) from the pages it has left, 3 for four
+ *                        or more down to 0 on its last; 2 sets it from the
+ *                        wave's index in its work-group (int8 body w, exact
+ *                        body 3 - w).  Outputs must be bit-identical to 0:
+ *                        only the interleaving of the waves changes, which
+ *                        exposes instruction hazards and races that the
+ *                        default interleaving hides.
  * NULL restores the plan.  The workspace size queries follow the same
  * setting, so change it only between a query and the calls it sized.
  * Results do not depend on the shape beyond FP32 rounding order (and, for
  * pv_fp16, the weights' rounding: 22 significant bits either way).
- * Errors: AKV_ERR_ARG for a negative field, one beyond its limit or pv_fp16
- * other than 0 or 1 (nothing is changed then).
+ * Errors: AKV_ERR_ARG for a negative field, one beyond its limit, pv_fp16
+ * other than 0 or 1 or issue_priority other than 0, 1 or 2 (nothing is
+ * changed then).
  */
 typedef struct {
     int32_t pages_per_split;
@@ -137,6 +149,7 @@ typedef struct {
     int32_t hybrid_int8_pages;
     int32_t hybrid_window_pages;
     int32_t pv_fp16;
+    int32_t issue_priority;
 } akv_launch_shape;
 akv_status akv_set_launch_shape(const akv_launch_shape *shape);
 

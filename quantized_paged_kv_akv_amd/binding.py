@@ -38,7 +38,7 @@ class akv_dims(ctypes.Structure):
 
 class akv_launch_shape(ctypes.Structure):
     _fields_ = [("pages_per_split", _i32), ("pages_per_wave", _i32), ("hybrid_int8_pages", _i32),
-                ("hybrid_window_pages", _i32), ("pv_fp16", _i32)]
+                ("hybrid_window_pages", _i32), ("pv_fp16", _i32), ("issue_priority", _i32)]
 
 
 def dims(num_kv_heads: int, group: int, head_dim: int = 256, page_size: int = 64) -> akv_dims:
@@ -141,13 +141,15 @@ def akv_set_profile_events(start_event=None, stop_event=None):
 
 
 def akv_set_launch_shape(pages_per_split: int = 0, pages_per_wave: int = 0, hybrid_int8_pages: int = 0,
-                         hybrid_window_pages: int = 0, pv_fp16: int = 0, reset: bool = False):
+                         hybrid_window_pages: int = 0, pv_fp16: int = 0, issue_priority: int = 0,
+                         reset: bool = False):
     """Launch-shape override of the calling thread (0 = planned); reset=True
     (or all zero) restores the library's plan."""
     if reset:
         _check("akv_set_launch_shape", _lib.akv_set_launch_shape(None))
         return
-    s = akv_launch_shape(pages_per_split, pages_per_wave, hybrid_int8_pages, hybrid_window_pages, pv_fp16)
+    s = akv_launch_shape(pages_per_split, pages_per_wave, hybrid_int8_pages, hybrid_window_pages, pv_fp16,
+                         issue_priority)
     _check("akv_set_launch_shape", _lib.akv_set_launch_shape(ctypes.byref(s)))
 
 

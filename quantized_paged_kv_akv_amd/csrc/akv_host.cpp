@@ -24,10 +24,11 @@ void clear_error() { g_err[0] = '\0'; }
 static thread_local hipEvent_t g_prof_start = nullptr;
 static thread_local hipEvent_t g_prof_stop = nullptr;
 // launch-shape overrides of the calling thread (akv_set_launch_shape); 0 = planned
-static thread_local akv_launch_shape g_shape = {0, 0, 0, 0, 0};
+static thread_local akv_launch_shape g_shape = {0, 0, 0, 0, 0, 0};
 
 hipEvent_t prof_start_event() { return g_prof_start; }
 bool pv_fp16() { return g_shape.pv_fp16 != 0; }
+int issue_priority() { return g_shape.issue_priority; }
 hipEvent_t prof_stop_event() { return g_prof_stop; }
 
 akv_status check_dims(const akv_dims* d) {
@@ -197,13 +198,15 @@ extern "C" akv_status akv_set_profile_events(void* start_event, void* stop_event
 extern "C" akv_status akv_set_launch_shape(const akv_launch_shape* shape) {
     akv::clear_error();
     if (!shape) {
-        akv::g_shape = akv_launch_shape{0, 0, 0, 0, 0};
+        akv::g_shape = akv_launch_shape{0, 0, 0, 0, 0, 0};
         return AKV_OK;
     }
     if (shape->pages_per_split < 0 || shape->pages_per_wave < 0 || shape->hybrid_int8_pages < 0 ||
         shape->hybrid_window_pages < 0)
         return akv::fail(AKV_ERR_ARG, "launch shape fields must be >= 0 (0 = planned)");
     if (shape->pv_fp16 != 0 && shape->pv_fp16 != 1) return akv::fail(AKV_ERR_ARG, "pv_fp16 must be 0 or 1");
+    if (shape->issue_priority < 0 || shape->issue_priority > 2)
+        return akv::fail(AKV_ERR_ARG, "issue_priority must be 0, 1 or 2");
     if (shape->pages_per_wave > akv::kMaxPagesPerWave || shape->hybrid_int8_pages > 4 * akv::kMaxPagesPerWave)
         return akv::fail(AKV_ERR_ARG, "launch shape beyond %d pages per wave (%d per int8 work-group)",
                          akv::kMaxPagesPerWave, 4 * akv::kMaxPagesPerWave);

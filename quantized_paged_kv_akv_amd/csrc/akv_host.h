@@ -23,6 +23,8 @@ hipEvent_t prof_start_event();
 hipEvent_t prof_stop_event();
 // the calling thread's launch shape asks for the FP16 PV operand of the int8 tier
 bool pv_fp16();
+// the calling thread's wave issue-priority probe (0 = off, 1 = by pages left, 2 = by wave)
+int issue_priority();
 
 // Shape checks common to every attention/quantize call.
 akv_status check_dims(const akv_dims* d);

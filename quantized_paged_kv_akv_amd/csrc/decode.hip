@@ -82,6 +82,24 @@ struct ExactArgs {
     float* part_lse;
 };
 
+// Wave issue-priority probe of akv_set_launch_shape, a template argument of
+// the decode bodies (the default instantiation, 0, carries no code for it):
+// 1 sets each wave's priority from the pages it has left, 2 from its index in
+// the work-group.
+constexpr int kPrioOff = 0, kPrioPagesLeft = 1, kPrioWave = 2;
+
+// The wave's issue priority (s_setprio takes only an immediate).  Used by the
+// scheduling probe of akv_set_launch_shape, which perturbs how the waves of a
+// compute unit interleave without changing what any wave computes.
+__device__ __forceinline__ void set_issue_priority(int level) {
+    switch (level) {
+        case 0: __builtin_amdgcn_s_setprio(0); break;
+        case 1: __builtin_amdgcn_s_setprio(1); break;
+        case 2: __builtin_amdgcn_s_setprio(2); break;
+        default: __builtin_amdgcn_s_setprio(3); break;
+    }
+}
+
 // LDS of the exact tier's body
 struct ExactSmem {
     float part[2][4][16][64];  // QK partial logits of the four waves, double-buffered
@@ -220,7 +238,7 @@ struct Int8Smem {
 constexpr int kPvF16 = 0;
 constexpr int kPvI8 = 3;
 
-template <int PvLimbs>
+template <int PvLimbs, int Prio>
 __device__ __forceinline__ void int8_split(const Int8Args& a, Int8Smem& sm, int split, int kvh, int b) {
     const int np = min(a.n_pages[b], a.max_pages);
     // this work-group's pages [wg0, wg0 + len): a near-equal share of the request's
@@ -232,6 +250,7 @@ __device__ __forceinline__ void int8_split(const Int8Args& a, Int8Smem& sm, int 
     }
     const int tid = threadIdx.x, l = tid & 63, n = l & 15, g = l >> 4;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+    if constexpr (Prio == kPrioWave) set_issue_priority(w);
     const int G = a.G, Hkv = a.Hkv, Hq = Hkv * G;
     // MFMA column n carries head n >> 1: the FP16 hi part in even columns, the
     // lo part in odd ones (adjacent lanes add them back together)
@@ -320,6 +339,7 @@ __device__ __forceinline__ void int8_split(const Int8Args& a, Int8Smem& sm, int 
 
         auto page = [&](auto prefetch, int p) {
             constexpr bool PF = decltype(prefetch)::value;
+            if constexpr (Prio == kPrioPagesLeft) set_issue_priority(min(3, pb - p - 1));
             const int slot = (p - pa) & 1;
             const float* scl = sm.sc[w][slot];
             size_t nb = 0, ns = 0;
@@ -655,7 +675,7 @@ struct L13Source {
     }
 };
 
-template <class Src>
+template <int Prio, class Src>
 __device__ __forceinline__ void exact_split(const ExactArgs& a, const Src& src, ExactSmem& sm, int split, int kvh,
                                             int b) {
     const int len = a.seq_len[b];
@@ -667,6 +687,7 @@ __device__ __forceinline__ void exact_split(const ExactArgs& a, const Src& src, 
     }
     const int p1 = min(np, p0 + a.pps);
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, n = l & 15, g = l >> 4;
+    if constexpr (Prio == kPrioWave) set_issue_priority(3 - __builtin_amdgcn_readfirstlane(w));
     const int hh = n & 7;
     const bool hi_lane = n < 8;
     const bool valid = hh < a.G;
@@ -700,6 +721,7 @@ __device__ __forceinline__ void exact_split(const ExactArgs& a, const Src& src, 
 
     int it = 0;
     for (int p = p0; p < p1; ++p, ++it) {
+        if constexpr (Prio == kPrioPagesLeft) set_issue_priority(min(3, p1 - p - 1));
         const bool has_next = p + 1 < p1;
         typename Src::Page nxt;
         if (has_next) src.load(pt[p + 1], kvh, Hkv, w, l, nxt);
@@ -758,24 +780,26 @@ union SplitSmem {
     } bx;
 };
 
-template <int PvLimbs>
+template <int PvLimbs, int Prio>
 __global__ __launch_bounds__(kThreads, 2) void decode_int8_kernel(Int8Args a) {
     __shared__ Int8Smem sm;
-    int8_split<PvLimbs>(a, sm, blockIdx.x, blockIdx.y, blockIdx.z);
+    int8_split<PvLimbs, Prio>(a, sm, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
+template <int Prio>
 __global__ __launch_bounds__(kThreads, 2) void decode_exact_kernel(ExactArgs a) {
     __shared__ ExactSmem sm;
     __shared__ Bf16Stage st;
-    exact_split(a, Bf16Source{a.kb, a.vb, st.q[threadIdx.x >> 6]}, sm, blockIdx.x, blockIdx.y, blockIdx.z);
+    exact_split<Prio>(a, Bf16Source{a.kb, a.vb, st.q[threadIdx.x >> 6]}, sm, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 // The exact body over lossless 13-bit planes: same split plan and
 // arithmetic as decode_exact_kernel, so the result is bit-identical to it on
 // the decoded pages.
+template <int Prio>
 __global__ __launch_bounds__(kThreads, 2) void decode_l13_kernel(ExactArgs a, L13Source src) {
     __shared__ ExactSmem sm;
-    exact_split(a, src, sm, blockIdx.x, blockIdx.y, blockIdx.z);
+    exact_split<Prio>(a, src, sm, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 // Both tiers of a layer in one launch: in each (request, KV head) row of the
@@ -783,15 +807,15 @@ __global__ __launch_bounds__(kThreads, 2) void decode_l13_kernel(ExactArgs a, L1
 // (measured against window-first: the same at 128K, 2 us faster per 32K step,
 // 0.8% faster batched); all write partial columns of the same rows (int8
 // columns first, window columns after them).
-template <int PvLimbs>
+template <int PvLimbs, int Prio>
 __global__ __launch_bounds__(kThreads, 2) void decode_hybrid_kernel(Int8Args a8, ExactArgs ax, int nw) {
     __shared__ SplitSmem sm;
     const int n8s = (int)gridDim.x - nw;
     if ((int)blockIdx.x >= n8s)
-        exact_split(ax, Bf16Source{ax.kb, ax.vb, sm.bx.st.q[threadIdx.x >> 6]}, sm.bx.ex, blockIdx.x - n8s, blockIdx.y,
-                    blockIdx.z);
+        exact_split<Prio>(ax, Bf16Source{ax.kb, ax.vb, sm.bx.st.q[threadIdx.x >> 6]}, sm.bx.ex, blockIdx.x - n8s,
+                          blockIdx.y, blockIdx.z);
     else
-        int8_split<PvLimbs>(a8, sm.i8, blockIdx.x, blockIdx.y, blockIdx.z);
+        int8_split<PvLimbs, Prio>(a8, sm.i8, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 // Tensors: non-NULL and 16-byte aligned.  int32 page tables and length
@@ -950,10 +974,14 @@ extern "C" akv_status akv_decode_attn_int8(const akv_dims* dims, int32_t batch, 
                            softmax_scale, plan);
     split_workspace(dims, batch, plan.n_splits, workspace, &a.part_o, &a.part_lse);
     dim3 grid((unsigned)plan.n_splits, (unsigned)dims->num_kv_heads, (unsigned)batch);
-    if (pv_fp16())
-        launch_split(decode_int8_kernel<kPvF16>, grid, s, a);
-    else
-        launch_split(decode_int8_kernel<kPvI8>, grid, s, a);
+    switch (pv_fp16() ? 3 + issue_priority() : issue_priority()) {
+        case 0: launch_split(decode_int8_kernel<kPvI8, kPrioOff>, grid, s, a); break;
+        case 1: launch_split(decode_int8_kernel<kPvI8, kPrioPagesLeft>, grid, s, a); break;
+        case 2: launch_split(decode_int8_kernel<kPvI8, kPrioWave>, grid, s, a); break;
+        case 3: launch_split(decode_int8_kernel<kPvF16, kPrioOff>, grid, s, a); break;
+        case 4: launch_split(decode_int8_kernel<kPvF16, kPrioPagesLeft>, grid, s, a); break;
+        default: launch_split(decode_int8_kernel<kPvF16, kPrioWave>, grid, s, a); break;
+    }
     if ((st = launch_status("decode_int8_kernel")) != AKV_OK) return st;
     return launch_combine(rows, dims->head_dim, a.part_o, a.part_lse, plan.n_splits, out_o, out_lse, s);
 }
@@ -978,7 +1006,11 @@ extern "C" akv_status akv_decode_attn_exact(const akv_dims* dims, int32_t batch,
     ExactArgs a = exact_args(dims, q, k_bf16, v_bf16, page_table, seq_len, max_pages, softmax_scale, plan);
     split_workspace(dims, batch, plan.n_splits, workspace, &a.part_o, &a.part_lse);
     dim3 grid((unsigned)plan.n_splits, (unsigned)dims->num_kv_heads, (unsigned)batch);
-    launch_split(decode_exact_kernel, grid, s, a);
+    switch (issue_priority()) {
+        case 0: launch_split(decode_exact_kernel<kPrioOff>, grid, s, a); break;
+        case 1: launch_split(decode_exact_kernel<kPrioPagesLeft>, grid, s, a); break;
+        default: launch_split(decode_exact_kernel<kPrioWave>, grid, s, a); break;
+    }
     if ((st = launch_status("decode_exact_kernel")) != AKV_OK) return st;
     return launch_combine(rows, dims->head_dim, a.part_o, a.part_lse, plan.n_splits, out_o, out_lse, s);
 }
@@ -1041,10 +1073,14 @@ static akv_status decode_hybrid_impl(const akv_dims* dims, int32_t batch, const 
     ax.part_o = a8.part_o;
     ax.part_lse = a8.part_lse;
     dim3 grid((unsigned)n_cols, (unsigned)dims->num_kv_heads, (unsigned)batch);
-    if (pv_fp16())
-        launch_split(decode_hybrid_kernel<kPvF16>, grid, s, a8, ax, pw.n_splits);
-    else
-        launch_split(decode_hybrid_kernel<kPvI8>, grid, s, a8, ax, pw.n_splits);
+    switch (pv_fp16() ? 3 + issue_priority() : issue_priority()) {
+        case 0: launch_split(decode_hybrid_kernel<kPvI8, kPrioOff>, grid, s, a8, ax, pw.n_splits); break;
+        case 1: launch_split(decode_hybrid_kernel<kPvI8, kPrioPagesLeft>, grid, s, a8, ax, pw.n_splits); break;
+        case 2: launch_split(decode_hybrid_kernel<kPvI8, kPrioWave>, grid, s, a8, ax, pw.n_splits); break;
+        case 3: launch_split(decode_hybrid_kernel<kPvF16, kPrioOff>, grid, s, a8, ax, pw.n_splits); break;
+        case 4: launch_split(decode_hybrid_kernel<kPvF16, kPrioPagesLeft>, grid, s, a8, ax, pw.n_splits); break;
+        default: launch_split(decode_hybrid_kernel<kPvF16, kPrioWave>, grid, s, a8, ax, pw.n_splits); break;
+    }
     if ((st = launch_status("decode_hybrid_kernel")) != AKV_OK) return st;
     return launch_combine(rows, dims->head_dim, a8.part_o, a8.part_lse, n_cols, out_o, out_lse, s);
 }
@@ -1101,7 +1137,11 @@ extern "C" akv_status akv_decode_attn_l13(const akv_dims* dims, int32_t batch, c
     split_workspace(dims, batch, plan.n_splits, workspace, &a.part_o, &a.part_lse);
     const L13Source src{l13_arena, l13_desc, l13_table};
     dim3 grid((unsigned)plan.n_splits, (unsigned)dims->num_kv_heads, (unsigned)batch);
-    launch_split(decode_l13_kernel, grid, s, a, src);
+    switch (issue_priority()) {
+        case 0: launch_split(decode_l13_kernel<kPrioOff>, grid, s, a, src); break;
+        case 1: launch_split(decode_l13_kernel<kPrioPagesLeft>, grid, s, a, src); break;
+        default: launch_split(decode_l13_kernel<kPrioWave>, grid, s, a, src); break;
+    }
     if ((st = launch_status("decode_l13_kernel")) != AKV_OK) return st;
     return launch_combine(rows, dims->head_dim, a.part_o, a.part_lse, plan.n_splits, out_o, out_lse, s);
 }

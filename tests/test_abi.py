@@ -126,8 +126,10 @@ def test_launch_shape_validation(B):
     lib = B._lib
     d = B.dims(4, 6)
     planned = B.akv_decode_workspace_bytes(d, 1, 2032)
+    planned_h = B.akv_decode_hybrid_workspace_bytes(d, 1, 2032, 16)
     for bad in (dict(pages_per_split=-1), dict(pages_per_wave=65), dict(hybrid_int8_pages=257),
-                dict(hybrid_window_pages=-3), dict(pv_fp16=2), dict(pv_fp16=-1)):
+                dict(hybrid_window_pages=-3), dict(pv_fp16=2), dict(pv_fp16=-1), dict(issue_priority=3),
+                dict(issue_priority=-1)):
         with pytest.raises(B.AkvError) as e:
             B.akv_set_launch_shape(**bad)
         assert e.value.status_name == "AKV_ERR_ARG"
@@ -139,9 +141,13 @@ def test_launch_shape_validation(B):
         B.akv_set_launch_shape(hybrid_int8_pages=8, hybrid_window_pages=1)
         need = B.akv_decode_hybrid_workspace_bytes(d, 1, 2032, 16)
         assert need >= 24 * (254 + 16) * 257 * 4
-        # the PV operand choice does not change the plan
+        # the PV operand choice and the issue-priority probe do not change the plan
         B.akv_set_launch_shape(pv_fp16=1)
         assert B.akv_decode_workspace_bytes(d, 1, 2032) == planned
+        for prio in (1, 2):
+            B.akv_set_launch_shape(issue_priority=prio)
+            assert B.akv_decode_workspace_bytes(d, 1, 2032) == planned
+            assert B.akv_decode_hybrid_workspace_bytes(d, 1, 2032, 16) == planned_h
     finally:
         B.akv_set_launch_shape(reset=True)
     assert B.akv_decode_workspace_bytes(d, 1, 2032) == planned

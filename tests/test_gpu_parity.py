@@ -408,6 +408,60 @@ def test_batched_full_size(B):
     _hybrid_layer(B, w, d, "batched32")
 
 
+@pytest.mark.parametrize("case", ["ctx32k", "batched4"])
+def test_issue_priority_probe_keeps_outputs(B, case):
+    """The issue-priority probe (akv_set_launch_shape issue_priority 1: by
+    pages left, 2: by wave index) changes only how the waves of a compute unit
+    interleave, so the fused hybrid layer, the int8 tier alone and the exact
+    tier alone must give bit-identical outputs under it.  (A hand-written
+    conversion whose half-register writes were read by the very next
+    instruction passed every parity test at the default priorities and went
+    wrong under this probe.)"""
+    if case == "ctx32k":
+        w = configs.ctx32k()
+    else:
+        full = configs.batched()
+        w = inputs.Workload("batched4", full.cfg_id, batch=4, layers=1, num_kv_heads=4, group=6,
+                            lengths=full.lengths[:4], window=512, outlier_frac=0.02, permute=True)
+    d = inputs.make_layer_np(w, 7)
+    say("case issue-priority probe", case)
+    plan = d["plan"]
+    Hkv, G = w.num_kv_heads, w.group
+    src, dst = plan.quant_src_dst()
+    g = gpu_quantize(B, d["k_pool"], d["v_pool"], src, dst, max(1, plan.int8_slots_total), Hkv)
+    kpt, vpt = dev(d["k_pool"]), dev(d["v_pool"])
+    t8, tw = plan.int8_table(), plan.window_table()
+    n8, nw = dev(np.asarray(plan.n8, np.int32)), dev(np.asarray(plan.win_tokens, np.int32))
+    q, t8d, twd = dev(d["q"]), dev(t8), dev(tw)
+    d8 = B.dims(Hkv, G)
+    ws = torch.empty(max(16, B.akv_decode_hybrid_workspace_bytes(d8, w.batch, t8.shape[1], tw.shape[1])),
+                     dtype=torch.uint8, device="cuda")
+
+    def run_all():
+        ho = torch.full((w.batch, w.num_q_heads, 256), float("nan"), device="cuda")
+        hl = torch.full((w.batch, w.num_q_heads), float("nan"), device="cuda")
+        B.akv_decode_hybrid(d8, w.batch, q, g["k_codes"], g["v_codes"], g["k_chan"], g["k_tok"], g["v_chan"],
+                            t8d, n8, t8.shape[1], kpt, vpt, twd, nw, tw.shape[1], SIG, ho, hl, ws)
+        o8, l8 = run_int8(B, Hkv, G, d["q"], g, t8, plan.n8)
+        ow, lw = run_exact(B, Hkv, G, d["q"], kpt, vpt, tw, plan.win_tokens)
+        torch.cuda.synchronize()
+        return [x.clone() for x in (ho, hl, o8, l8, ow, lw)]
+
+    ref = run_all()
+    try:
+        for prio in (1, 2):
+            B.akv_set_launch_shape(issue_priority=prio)
+            got = run_all()
+            for name, a, b in zip(("hybrid O", "hybrid LSE", "int8 O", "int8 LSE", "exact O", "exact LSE"),
+                                  ref, got):
+                assert torch.equal(a, b), f"{case}: {name} changed under issue_priority={prio}"
+    finally:
+        B.akv_set_launch_shape(reset=True)
+    rows = w.batch * w.num_q_heads
+    rm, rlm = oracle_hybrid(O, Hkv, G, d["q"], g, t8, plan.n8, d["k_pool"], d["v_pool"], tw, plan.win_tokens)
+    check_attn(ref[0].view(rows, 256), ref[1].view(rows), rm, rlm, f"{case} hybrid (probe reference)")
+
+
 def test_hybrid_step_replays_from_a_graph(B):
     """A two-layer hybrid step captured in a HIP graph replays to the eager
     result, several times, with eager work and synchronisations between the
