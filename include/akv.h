@@ -221,7 +221,9 @@ size_t akv_decode_workspace_bytes(const akv_dims *dims, int32_t batch, int32_t m
  *
  * n_pages: int32 [batch] device array, each in [0, max_pages].
  * workspace: at least akv_decode_workspace_bytes(dims, batch, max_pages).
- * Errors: AKV_ERR_ARG, AKV_ERR_UNSUPPORTED, AKV_ERR_ALIGN, AKV_ERR_WORKSPACE.
+ * Errors: AKV_ERR_ARG, AKV_ERR_UNSUPPORTED (also when the split plan's
+ * work-groups per request times max_pages reach 2^32, never below 65,536
+ * pages), AKV_ERR_ALIGN, AKV_ERR_WORKSPACE.
  */
 akv_status akv_decode_attn_int8(const akv_dims *dims, int32_t batch, const uint16_t *q,
                                 const int8_t *k_codes, const int8_t *v_codes,
@@ -262,7 +264,8 @@ akv_status akv_decode_attn_exact(const akv_dims *dims, int32_t batch, const uint
  * counts); both empty gives O = 0, LSE = -inf.
  * workspace: at least akv_decode_hybrid_workspace_bytes(dims, batch,
  * max_pages_int8, max_pages_window).
- * Errors: AKV_ERR_ARG, AKV_ERR_UNSUPPORTED, AKV_ERR_ALIGN, AKV_ERR_WORKSPACE.
+ * Errors: AKV_ERR_ARG, AKV_ERR_UNSUPPORTED (as akv_decode_attn_int8 for the
+ * int8 tier's split plan), AKV_ERR_ALIGN, AKV_ERR_WORKSPACE.
  */
 size_t akv_decode_hybrid_workspace_bytes(const akv_dims *dims, int32_t batch, int32_t max_pages_int8,
                                          int32_t max_pages_window);

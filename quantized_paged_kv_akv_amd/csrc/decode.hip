@@ -241,9 +241,13 @@ constexpr int kPvI8 = 3;
 template <int PvLimbs, int Prio>
 __device__ __forceinline__ void int8_split(const Int8Args& a, Int8Smem& sm, int split, int kvh, int b) {
     const int np = min(a.n_pages[b], a.max_pages);
-    // this work-group's pages [wg0, wg0 + len): a near-equal share of the request's
-    const int wg0 = (int)((long long)split * np / a.splits);
-    const int len = (int)((long long)(split + 1) * np / a.splits) - wg0;
+    // this work-group's pages [wg0, wg0 + len): a near-equal share of the
+    // request's, in 32-bit arithmetic (the host refuses plans whose
+    // splits x max_pages reaches 2^32; the 64-bit divisions cost about 380
+    // scalar instructions before the first page-table read, 6 us per 128K
+    // step)
+    const int wg0 = (int)((uint32_t)split * (uint32_t)np / (uint32_t)a.splits);
+    const int len = (int)((uint32_t)(split + 1) * (uint32_t)np / (uint32_t)a.splits) - wg0;
     if (len <= 0) {
         write_empty(a.G, a.Hkv, kvh, b, a.n_cols, a.col0 + split, a.part_lse);
         return;
@@ -880,12 +884,17 @@ static Int8Args int8_args(const akv_dims* dims, const uint16_t* q, const int8_t*
 }
 
 // A wave stages at most kMaxPagesPerWave page slots in LDS: a work-group's
-// share, at most ceil(max_pages / n_splits) pages, must fit four waves.
+// share, at most ceil(max_pages / n_splits) pages, must fit four waves.  The
+// kernel computes the shares in 32-bit arithmetic: splits x max_pages must
+// stay below 2^32 (always so below 65,536 pages per table row).
 static akv_status check_int8_plan(const SplitPlan& p, int max_pages) {
     const long long per_wg = p.n_splits > 0 ? ((long long)max_pages + p.n_splits - 1) / p.n_splits : 0;
     if (p.n_splits < 1 || per_wg > 4 * kMaxPagesPerWave)
         return fail(AKV_ERR_ARG, "int8 split plan of %d splits for %d pages exceeds %d pages per work-group",
                     p.n_splits, max_pages, 4 * kMaxPagesPerWave);
+    if ((long long)p.n_splits * max_pages >= (1LL << 32))
+        return fail(AKV_ERR_UNSUPPORTED, "int8 split plan of %d splits for %d pages: splits x pages reaches 2^32",
+                    p.n_splits, max_pages);
     return AKV_OK;
 }
 

@@ -70,6 +70,17 @@ def test_host_side_validation(B):
     assert st == -3
     st = lib.akv_decode_attn_int8(ctypes.byref(d), 1, t4, p, p, p, p, p, t4, t4, 2032, 0.0625, p, p, p, 16, None)
     assert st == -3
+    # the kernel's page shares are 32-bit: splits x max_pages must stay below 2^32
+    try:
+        B.akv_set_launch_shape(pages_per_wave=1)  # 4 pages per work-group: 35,000 splits of 140,000 pages
+        st = lib.akv_decode_attn_int8(ctypes.byref(d), 1, p, p, p, p, p, p, t4, t4, 140000, 0.0625, p, p, p, 16,
+                                      None)
+        assert st == -2 and "2^32" in lib.akv_last_error().decode()
+        st = lib.akv_decode_attn_int8(ctypes.byref(d), 1, p, p, p, p, p, p, t4, t4, 60000, 0.0625, p, p, p, 16,
+                                      None)
+        assert st == -4  # 15,000 x 60,000 < 2^32: on to the workspace check
+    finally:
+        B.akv_set_launch_shape(reset=True)
     # ring refuses fewer than 2 slots and NULL slots
     h = ctypes.c_void_p()
     arr = (ctypes.c_void_p * 1)(ctypes.c_void_p(16))
