@@ -240,6 +240,16 @@ constexpr int kPvI8 = 3;
 
 template <int PvLimbs, int Prio>
 __device__ __forceinline__ void int8_split(const Int8Args& a, Int8Smem& sm, int split, int kvh, int b) {
+    // The wave's first page-table entry if the request fills its table row
+    // (the usual single-request case), read beside the page count rather than
+    // after it: one dependent round trip less before the first page streams
+    // (1.3 us less per 128K step).  The entry is used only if the real share
+    // starts where this guess does; the read stays inside the table row.
+    const int w_s = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int wg0_s = (int)((uint32_t)split * (uint32_t)a.max_pages / (uint32_t)a.splits);
+    int spec_slot = 0;
+    if (a.max_pages > 0)
+        spec_slot = a.page_table[(size_t)b * a.max_pages + min(wg0_s + w_s, a.max_pages - 1)];
     const int np = min(a.n_pages[b], a.max_pages);
     // this work-group's pages [wg0, wg0 + len): a near-equal share of the
     // request's, in 32-bit arithmetic (the host refuses plans whose
@@ -292,7 +302,8 @@ __device__ __forceinline__ void int8_split(const Int8Args& a, Int8Smem& sm, int 
     u32x4 sk0 = {0, 0, 0, 0}, sv0 = {0, 0, 0, 0};
     float st0 = 0.0f;
     if (cnt > 0) {
-        const size_t sb = (size_t)__builtin_amdgcn_readfirstlane(pt[pt_index(0)]) * Hkv + kvh;
+        const int s0 = (wg0 == wg0_s) ? spec_slot : pt[pt_index(0)];  // same entry when the shares agree
+        const size_t sb = (size_t)__builtin_amdgcn_readfirstlane(s0) * Hkv + kvh;
         const int8_t* kp = a.kc + sb * (kP * kD);
 #pragma unroll
         for (int s2 = 0; s2 < 4; ++s2)
