@@ -501,10 +501,12 @@ __device__ __forceinline__ void int8_split(const Int8Args& a, Int8Smem& sm, int 
         }
     }
     __syncthreads();
-    // item (h, 4 channels) per thread: a wave covers one head, so the per-wave
-    // statistics are broadcast reads and the O reads and stores are 16 bytes
-    for (int it = tid; it < G * (kD / 4); it += kThreads) {
-        const int h = it / (kD / 4), c4 = 4 * (it % (kD / 4));
+    // item (h, 8 channels) per thread: half a wave covers one head, so up to
+    // eight heads take one pass -- the merge is the tail of every
+    // work-group (two passes of 4 channels cost 4 us per 128K step and 6 per
+    // 32K step); O reads and stores are 16 bytes
+    for (int it = tid; it < G * (kD / 8); it += kThreads) {
+        const int h = it / (kD / 8), c8 = 8 * (it % (kD / 8));
         float mk[4], Ms = -INFINITY;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -512,18 +514,21 @@ __device__ __forceinline__ void int8_split(const Int8Args& a, Int8Smem& sm, int 
             Ms = fmaxf(Ms, mk[k]);
         }
         float lt = 0.0f;
-        f32x4 ot = {0.0f, 0.0f, 0.0f, 0.0f};
+        f32x4 o0 = {0.0f, 0.0f, 0.0f, 0.0f}, o1 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             if (mk[k] == -INFINITY) continue;
             const float f = exp2f(mk[k] - Ms);
             lt += f * sm.ml[k][h];
-            ot += f * *reinterpret_cast<const f32x4*>(&sm.mo[k][h][c4]);
+            o0 += f * *reinterpret_cast<const f32x4*>(&sm.mo[k][h][c8]);
+            o1 += f * *reinterpret_cast<const f32x4*>(&sm.mo[k][h][c8 + 4]);
         }
         const size_t row = row0 + h;
         const float inv = 1.0f / lt;
-        *reinterpret_cast<f32x4*>(&a.part_o[(row * a.n_cols + a.col0 + split) * kD + c4]) = ot * inv;
-        if (c4 == 0) a.part_lse[row * a.n_cols + a.col0 + split] = (Ms + log2f(lt)) * kLn2;
+        float* dst = &a.part_o[(row * a.n_cols + a.col0 + split) * kD + c8];
+        *reinterpret_cast<f32x4*>(dst) = o0 * inv;
+        *reinterpret_cast<f32x4*>(dst + 4) = o1 * inv;
+        if (c8 == 0) a.part_lse[row * a.n_cols + a.col0 + split] = (Ms + log2f(lt)) * kLn2;
     }
 }
 
