@@ -217,7 +217,7 @@ __device__ __forceinline__ void write_empty(int G, int Hkv, int kvh, int b, int 
 // go to the other half of a per-wave LDS double buffer.  A work-group owns a
 // near-equal share of one (request, KV head)'s pages; its four waves take
 // every fourth page of it and merge once at the end.
-struct Int8Smem {
+struct alignas(16) Int8Smem {  // 16-byte aligned: its f32x4 rows move as 16-byte LDS accesses
     float q[kMaxGroup][kD + 4];    // query rows (scaled by 2^-e per row), FP32; +4 spreads rows over banks
     float qe[kMaxGroup];           // the row's power-of-two exponent e
     float sc[4][2][2 * kD + kP];   // per wave, per slot: k_chan | v_chan | k_tok * scale_log2
