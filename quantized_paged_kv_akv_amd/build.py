@@ -24,6 +24,12 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",
     # no packed FP32 instructions anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # kernel-argument preloading: up to 16 dwords of leading scalar kernel
+    # arguments arrive in scalar registers at wave start instead of through a
+    # load from the argument buffer (the combine pass and the split kernels'
+    # first reads wait one round trip less; the code object keeps a prologue
+    # that loads them the old way where the firmware does not preload)
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-I", os.path.join(ROOT, "include"),
 ]
 

@@ -69,6 +69,23 @@ struct Int8Args {
     float* part_lse;
 };
 
+// The int8 tier's first reads (the page count and the first page-table
+// entry) and its share arithmetic need only the page table, the page counts,
+// the table's row length and the split count.  The kernels take these four
+// again as leading scalar arguments, ahead of the argument structs, because
+// the library is built with kernel-argument preloading: leading scalar
+// arguments arrive in scalar registers when the wave starts, so the first
+// reads go out without waiting for a kernel-argument load (a struct argument
+// is never preloaded).
+__device__ __forceinline__ Int8Args with_lead(Int8Args a, const int32_t* page_table, const int32_t* n_pages,
+                                              int max_pages, int splits) {
+    a.page_table = page_table;
+    a.n_pages = n_pages;
+    a.max_pages = max_pages;
+    a.splits = splits;
+    return a;
+}
+
 struct ExactArgs {
     const uint16_t* q;
     const uint16_t* kb;
@@ -801,9 +818,11 @@ union SplitSmem {
 };
 
 template <int PvLimbs, int Prio>
-__global__ __launch_bounds__(kThreads, 2) void decode_int8_kernel(Int8Args a) {
+__global__ __launch_bounds__(kThreads, 2) void decode_int8_kernel(const int32_t* page_table, const int32_t* n_pages,
+                                                                  int max_pages, int splits, Int8Args a) {
     __shared__ Int8Smem sm;
-    int8_split<PvLimbs, Prio>(a, sm, blockIdx.x, blockIdx.y, blockIdx.z);
+    int8_split<PvLimbs, Prio>(with_lead(a, page_table, n_pages, max_pages, splits), sm, blockIdx.x, blockIdx.y,
+                              blockIdx.z);
 }
 
 template <int Prio>
@@ -828,14 +847,16 @@ __global__ __launch_bounds__(kThreads, 2) void decode_l13_kernel(ExactArgs a, L1
 // 0.8% faster batched); all write partial columns of the same rows (int8
 // columns first, window columns after them).
 template <int PvLimbs, int Prio>
-__global__ __launch_bounds__(kThreads, 2) void decode_hybrid_kernel(Int8Args a8, ExactArgs ax, int nw) {
+__global__ __launch_bounds__(kThreads, 2) void decode_hybrid_kernel(const int32_t* page_table, const int32_t* n_pages,
+                                                                    int max_pages, int splits, int n8s, Int8Args a8,
+                                                                    ExactArgs ax) {
     __shared__ SplitSmem sm;
-    const int n8s = (int)gridDim.x - nw;
     if ((int)blockIdx.x >= n8s)
         exact_split<Prio>(ax, Bf16Source{ax.kb, ax.vb, sm.bx.st.q[threadIdx.x >> 6]}, sm.bx.ex, blockIdx.x - n8s,
                           blockIdx.y, blockIdx.z);
     else
-        int8_split<PvLimbs, Prio>(a8, sm.i8, blockIdx.x, blockIdx.y, blockIdx.z);
+        int8_split<PvLimbs, Prio>(with_lead(a8, page_table, n_pages, max_pages, splits), sm.i8, blockIdx.x, blockIdx.y,
+                                  blockIdx.z);
 }
 
 // Tensors: non-NULL and 16-byte aligned.  int32 page tables and length
@@ -972,6 +993,13 @@ static void launch_split(void (*kernel)(A...), dim3 grid, hipStream_t s, A... ar
         kernel<<<grid, kThreads, 0, s>>>(args...);
 }
 
+// The int8 kernel with its leading copies of the struct's page table, page
+// counts, row length and split count (see with_lead).
+template <typename K>
+static void launch_int8(K kernel, dim3 grid, hipStream_t s, const Int8Args& a) {
+    launch_split(kernel, grid, s, a.page_table, a.n_pages, a.max_pages, a.splits, a);
+}
+
 }  // namespace akv
 
 using namespace akv;
@@ -1000,12 +1028,12 @@ extern "C" akv_status akv_decode_attn_int8(const akv_dims* dims, int32_t batch, 
     split_workspace(dims, batch, plan.n_splits, workspace, &a.part_o, &a.part_lse);
     dim3 grid((unsigned)plan.n_splits, (unsigned)dims->num_kv_heads, (unsigned)batch);
     switch (pv_fp16() ? 3 + issue_priority() : issue_priority()) {
-        case 0: launch_split(decode_int8_kernel<kPvI8, kPrioOff>, grid, s, a); break;
-        case 1: launch_split(decode_int8_kernel<kPvI8, kPrioPagesLeft>, grid, s, a); break;
-        case 2: launch_split(decode_int8_kernel<kPvI8, kPrioWave>, grid, s, a); break;
-        case 3: launch_split(decode_int8_kernel<kPvF16, kPrioOff>, grid, s, a); break;
-        case 4: launch_split(decode_int8_kernel<kPvF16, kPrioPagesLeft>, grid, s, a); break;
-        default: launch_split(decode_int8_kernel<kPvF16, kPrioWave>, grid, s, a); break;
+        case 0: launch_int8(decode_int8_kernel<kPvI8, kPrioOff>, grid, s, a); break;
+        case 1: launch_int8(decode_int8_kernel<kPvI8, kPrioPagesLeft>, grid, s, a); break;
+        case 2: launch_int8(decode_int8_kernel<kPvI8, kPrioWave>, grid, s, a); break;
+        case 3: launch_int8(decode_int8_kernel<kPvF16, kPrioOff>, grid, s, a); break;
+        case 4: launch_int8(decode_int8_kernel<kPvF16, kPrioPagesLeft>, grid, s, a); break;
+        default: launch_int8(decode_int8_kernel<kPvF16, kPrioWave>, grid, s, a); break;
     }
     if ((st = launch_status("decode_int8_kernel")) != AKV_OK) return st;
     return launch_combine(rows, dims->head_dim, a.part_o, a.part_lse, plan.n_splits, out_o, out_lse, s);
@@ -1099,12 +1127,12 @@ static akv_status decode_hybrid_impl(const akv_dims* dims, int32_t batch, const 
     ax.part_lse = a8.part_lse;
     dim3 grid((unsigned)n_cols, (unsigned)dims->num_kv_heads, (unsigned)batch);
     switch (pv_fp16() ? 3 + issue_priority() : issue_priority()) {
-        case 0: launch_split(decode_hybrid_kernel<kPvI8, kPrioOff>, grid, s, a8, ax, pw.n_splits); break;
-        case 1: launch_split(decode_hybrid_kernel<kPvI8, kPrioPagesLeft>, grid, s, a8, ax, pw.n_splits); break;
-        case 2: launch_split(decode_hybrid_kernel<kPvI8, kPrioWave>, grid, s, a8, ax, pw.n_splits); break;
-        case 3: launch_split(decode_hybrid_kernel<kPvF16, kPrioOff>, grid, s, a8, ax, pw.n_splits); break;
-        case 4: launch_split(decode_hybrid_kernel<kPvF16, kPrioPagesLeft>, grid, s, a8, ax, pw.n_splits); break;
-        default: launch_split(decode_hybrid_kernel<kPvF16, kPrioWave>, grid, s, a8, ax, pw.n_splits); break;
+        case 0: launch_split(decode_hybrid_kernel<kPvI8, kPrioOff>, grid, s, a8.page_table, a8.n_pages, a8.max_pages, a8.splits, n_cols - pw.n_splits, a8, ax); break;
+        case 1: launch_split(decode_hybrid_kernel<kPvI8, kPrioPagesLeft>, grid, s, a8.page_table, a8.n_pages, a8.max_pages, a8.splits, n_cols - pw.n_splits, a8, ax); break;
+        case 2: launch_split(decode_hybrid_kernel<kPvI8, kPrioWave>, grid, s, a8.page_table, a8.n_pages, a8.max_pages, a8.splits, n_cols - pw.n_splits, a8, ax); break;
+        case 3: launch_split(decode_hybrid_kernel<kPvF16, kPrioOff>, grid, s, a8.page_table, a8.n_pages, a8.max_pages, a8.splits, n_cols - pw.n_splits, a8, ax); break;
+        case 4: launch_split(decode_hybrid_kernel<kPvF16, kPrioPagesLeft>, grid, s, a8.page_table, a8.n_pages, a8.max_pages, a8.splits, n_cols - pw.n_splits, a8, ax); break;
+        default: launch_split(decode_hybrid_kernel<kPvF16, kPrioWave>, grid, s, a8.page_table, a8.n_pages, a8.max_pages, a8.splits, n_cols - pw.n_splits, a8, ax); break;
     }
     if ((st = launch_status("decode_hybrid_kernel")) != AKV_OK) return st;
     return launch_combine(rows, dims->head_dim, a8.part_o, a8.part_lse, n_cols, out_o, out_lse, s);
