@@ -44,16 +44,18 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
-    """Hash of the sources that decide the decode kernel's code and launch
-    shape, with comments and blank lines removed (a comment edit does not
-    change the kernel)."""
+    """Hash of the sources and compiler flags that decide the decode
+    kernel's code and launch shape, with comments and blank lines removed (a
+    comment edit does not change the kernel)."""
     import re
+    from quantized_paged_kv_akv_amd import build as akv_build
     h = hashlib.sha256()
     for f in ("decode.hip", "akv_device.h", "akv_host.cpp"):
         text = open(os.path.join(ROOT, "quantized_paged_kv_akv_amd", "csrc", f)).read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
         text = re.sub(r"//[^\n]*", "", text)
         h.update("\n".join(line.rstrip() for line in text.splitlines() if line.strip()).encode())
+    h.update(" ".join(f for f in akv_build.FLAGS if not f.startswith("/")).encode())
     return h.hexdigest()[:16]
 
 
