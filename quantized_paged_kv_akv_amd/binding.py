@@ -127,6 +127,11 @@ def _ptr(t: Optional[torch.Tensor], dtypes, name: str) -> _vp:
 
 
 _BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+_WS = (torch.uint8, torch.int8, torch.float32)
+
+
+def _ws_bytes(workspace) -> int:
+    return workspace.numel() * workspace.element_size() if workspace is not None else 0
 
 
 def version() -> str:
@@ -167,48 +172,68 @@ def akv_decode_workspace_bytes(d: akv_dims, batch: int, max_pages: int) -> int:
     return int(_lib.akv_decode_workspace_bytes(ctypes.byref(d), batch, max_pages))
 
 
+def _args_decode_attn_int8(d: akv_dims, batch: int, q, k_codes, v_codes, k_chan, k_tok, v_chan, page_table,
+                           n_pages, max_pages: int, softmax_scale: float, out_o, out_lse, workspace, stream=None):
+    return (ctypes.byref(d), batch, _ptr(q, _BF16, "q"), _ptr(k_codes, torch.int8, "k_codes"),
+            _ptr(v_codes, torch.int8, "v_codes"), _ptr(k_chan, torch.float32, "k_chan"),
+            _ptr(k_tok, torch.float32, "k_tok"), _ptr(v_chan, torch.float32, "v_chan"),
+            _ptr(page_table, torch.int32, "page_table"), _ptr(n_pages, torch.int32, "n_pages"), max_pages,
+            softmax_scale, _ptr(out_o, torch.float32, "out_o"), _ptr(out_lse, torch.float32, "out_lse"),
+            _ptr(workspace, _WS, "workspace"), _ws_bytes(workspace), _stream(stream))
+
+
 def akv_decode_attn_int8(d: akv_dims, batch: int, q, k_codes, v_codes, k_chan, k_tok, v_chan, page_table,
                          n_pages, max_pages: int, softmax_scale: float, out_o, out_lse, workspace,
                          stream=None):
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check("akv_decode_attn_int8", _lib.akv_decode_attn_int8(
-        ctypes.byref(d), batch, _ptr(q, _BF16, "q"), _ptr(k_codes, torch.int8, "k_codes"),
-        _ptr(v_codes, torch.int8, "v_codes"), _ptr(k_chan, torch.float32, "k_chan"),
-        _ptr(k_tok, torch.float32, "k_tok"), _ptr(v_chan, torch.float32, "v_chan"),
-        _ptr(page_table, torch.int32, "page_table"), _ptr(n_pages, torch.int32, "n_pages"), max_pages,
-        softmax_scale, _ptr(out_o, torch.float32, "out_o"), _ptr(out_lse, torch.float32, "out_lse"),
-        _ptr(workspace, (torch.uint8, torch.int8, torch.float32), "workspace"), ws_bytes, _stream(stream)))
+    _check("akv_decode_attn_int8", _lib.akv_decode_attn_int8(*_args_decode_attn_int8(
+        d, batch, q, k_codes, v_codes, k_chan, k_tok, v_chan, page_table, n_pages, max_pages, softmax_scale,
+        out_o, out_lse, workspace, stream)))
+
+
+
+def _args_decode_attn_exact(d: akv_dims, batch: int, q, k_bf16, v_bf16, page_table, seq_len, max_pages: int,
+                            softmax_scale: float, out_o, out_lse, workspace, stream=None):
+    return (ctypes.byref(d), batch, _ptr(q, _BF16, "q"), _ptr(k_bf16, _BF16, "k_bf16"),
+            _ptr(v_bf16, _BF16, "v_bf16"), _ptr(page_table, torch.int32, "page_table"),
+            _ptr(seq_len, torch.int32, "seq_len"), max_pages, softmax_scale,
+            _ptr(out_o, torch.float32, "out_o"), _ptr(out_lse, torch.float32, "out_lse"),
+            _ptr(workspace, _WS, "workspace"), _ws_bytes(workspace), _stream(stream))
 
 
 def akv_decode_attn_exact(d: akv_dims, batch: int, q, k_bf16, v_bf16, page_table, seq_len, max_pages: int,
                           softmax_scale: float, out_o, out_lse, workspace, stream=None):
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check("akv_decode_attn_exact", _lib.akv_decode_attn_exact(
-        ctypes.byref(d), batch, _ptr(q, _BF16, "q"), _ptr(k_bf16, _BF16, "k_bf16"),
-        _ptr(v_bf16, _BF16, "v_bf16"), _ptr(page_table, torch.int32, "page_table"),
-        _ptr(seq_len, torch.int32, "seq_len"), max_pages, softmax_scale,
-        _ptr(out_o, torch.float32, "out_o"), _ptr(out_lse, torch.float32, "out_lse"),
-        _ptr(workspace, (torch.uint8, torch.int8, torch.float32), "workspace"), ws_bytes, _stream(stream)))
+    _check("akv_decode_attn_exact", _lib.akv_decode_attn_exact(*_args_decode_attn_exact(
+        d, batch, q, k_bf16, v_bf16, page_table, seq_len, max_pages, softmax_scale, out_o, out_lse, workspace,
+        stream)))
+
 
 
 def akv_decode_hybrid_workspace_bytes(d: akv_dims, batch: int, max_pages_int8: int, max_pages_window: int) -> int:
     return int(_lib.akv_decode_hybrid_workspace_bytes(ctypes.byref(d), batch, max_pages_int8, max_pages_window))
 
 
+def _args_decode_hybrid(d: akv_dims, batch: int, q, k_codes, v_codes, k_chan, k_tok, v_chan, page_table_int8,
+                        n_pages_int8, max_pages_int8: int, k_bf16, v_bf16, page_table_window, window_len,
+                        max_pages_window: int, softmax_scale: float, out_o, out_lse, workspace, stream=None):
+    return (ctypes.byref(d), batch, _ptr(q, _BF16, "q"), _ptr(k_codes, torch.int8, "k_codes"),
+            _ptr(v_codes, torch.int8, "v_codes"), _ptr(k_chan, torch.float32, "k_chan"),
+            _ptr(k_tok, torch.float32, "k_tok"), _ptr(v_chan, torch.float32, "v_chan"),
+            _ptr(page_table_int8, torch.int32, "page_table_int8"), _ptr(n_pages_int8, torch.int32, "n_pages_int8"),
+            max_pages_int8, _ptr(k_bf16, _BF16, "k_bf16"), _ptr(v_bf16, _BF16, "v_bf16"),
+            _ptr(page_table_window, torch.int32, "page_table_window"), _ptr(window_len, torch.int32, "window_len"),
+            max_pages_window, softmax_scale, _ptr(out_o, torch.float32, "out_o"),
+            _ptr(out_lse, torch.float32, "out_lse"), _ptr(workspace, _WS, "workspace"), _ws_bytes(workspace),
+            _stream(stream))
+
+
 def akv_decode_hybrid(d: akv_dims, batch: int, q, k_codes, v_codes, k_chan, k_tok, v_chan, page_table_int8,
                       n_pages_int8, max_pages_int8: int, k_bf16, v_bf16, page_table_window, window_len,
                       max_pages_window: int, softmax_scale: float, out_o, out_lse, workspace, stream=None):
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check("akv_decode_hybrid", _lib.akv_decode_hybrid(
-        ctypes.byref(d), batch, _ptr(q, _BF16, "q"), _ptr(k_codes, torch.int8, "k_codes"),
-        _ptr(v_codes, torch.int8, "v_codes"), _ptr(k_chan, torch.float32, "k_chan"),
-        _ptr(k_tok, torch.float32, "k_tok"), _ptr(v_chan, torch.float32, "v_chan"),
-        _ptr(page_table_int8, torch.int32, "page_table_int8"), _ptr(n_pages_int8, torch.int32, "n_pages_int8"),
-        max_pages_int8, _ptr(k_bf16, _BF16, "k_bf16"), _ptr(v_bf16, _BF16, "v_bf16"),
-        _ptr(page_table_window, torch.int32, "page_table_window"), _ptr(window_len, torch.int32, "window_len"),
-        max_pages_window, softmax_scale, _ptr(out_o, torch.float32, "out_o"),
-        _ptr(out_lse, torch.float32, "out_lse"),
-        _ptr(workspace, (torch.uint8, torch.int8, torch.float32), "workspace"), ws_bytes, _stream(stream)))
+    _check("akv_decode_hybrid", _lib.akv_decode_hybrid(*_args_decode_hybrid(
+        d, batch, q, k_codes, v_codes, k_chan, k_tok, v_chan, page_table_int8, n_pages_int8, max_pages_int8,
+        k_bf16, v_bf16, page_table_window, window_len, max_pages_window, softmax_scale, out_o, out_lse, workspace,
+        stream)))
+
 
 
 STATIC_SCRATCH_BYTES = 16 << 20  # AKV_STATIC_SCRATCH_BYTES
@@ -230,10 +255,15 @@ def akv_decode_hybrid_static(d: akv_dims, batch: int, q, k_codes, v_codes, k_cha
         _ptr(out_lse, torch.float32, "out_lse"), _stream(stream)))
 
 
+def _args_merge_lse(rows: int, head_dim: int, acc_o, acc_lse, part_o, part_lse, stream=None):
+    return (rows, head_dim, _ptr(acc_o, torch.float32, "acc_o"), _ptr(acc_lse, torch.float32, "acc_lse"),
+            _ptr(part_o, torch.float32, "part_o"), _ptr(part_lse, torch.float32, "part_lse"), _stream(stream))
+
+
 def akv_merge_lse(rows: int, head_dim: int, acc_o, acc_lse, part_o, part_lse, stream=None):
-    _check("akv_merge_lse", _lib.akv_merge_lse(
-        rows, head_dim, _ptr(acc_o, torch.float32, "acc_o"), _ptr(acc_lse, torch.float32, "acc_lse"),
-        _ptr(part_o, torch.float32, "part_o"), _ptr(part_lse, torch.float32, "part_lse"), _stream(stream)))
+    _check("akv_merge_lse", _lib.akv_merge_lse(*_args_merge_lse(rows, head_dim, acc_o, acc_lse, part_o, part_lse,
+                                                                stream)))
+
 
 
 def akv_fill_empty(rows: int, head_dim: int, o, lse, stream=None):
@@ -267,15 +297,21 @@ def akv_l13_decode_pages(d: akv_dims, n: int, arena, desc, table, src_slot, dst_
         _stream(stream)))
 
 
+def _args_decode_attn_l13(d: akv_dims, batch: int, q, arena, desc, table, page_table, seq_len, max_pages: int,
+                          softmax_scale: float, out_o, out_lse, workspace, stream=None):
+    return (ctypes.byref(d), batch, _ptr(q, _BF16, "q"), _ptr(arena, torch.uint8, "arena"),
+            _ptr(desc, torch.int32, "desc"), _ptr(table, torch.uint8, "table"),
+            _ptr(page_table, torch.int32, "page_table"), _ptr(seq_len, torch.int32, "seq_len"), max_pages,
+            softmax_scale, _ptr(out_o, torch.float32, "out_o"), _ptr(out_lse, torch.float32, "out_lse"),
+            _ptr(workspace, _WS, "workspace"), _ws_bytes(workspace), _stream(stream))
+
+
 def akv_decode_attn_l13(d: akv_dims, batch: int, q, arena, desc, table, page_table, seq_len, max_pages: int,
                         softmax_scale: float, out_o, out_lse, workspace, stream=None):
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check("akv_decode_attn_l13", _lib.akv_decode_attn_l13(
-        ctypes.byref(d), batch, _ptr(q, _BF16, "q"), _ptr(arena, torch.uint8, "arena"),
-        _ptr(desc, torch.int32, "desc"), _ptr(table, torch.uint8, "table"),
-        _ptr(page_table, torch.int32, "page_table"), _ptr(seq_len, torch.int32, "seq_len"), max_pages,
-        softmax_scale, _ptr(out_o, torch.float32, "out_o"), _ptr(out_lse, torch.float32, "out_lse"),
-        _ptr(workspace, (torch.uint8, torch.int8, torch.float32), "workspace"), ws_bytes, _stream(stream)))
+    _check("akv_decode_attn_l13", _lib.akv_decode_attn_l13(*_args_decode_attn_l13(
+        d, batch, q, arena, desc, table, page_table, seq_len, max_pages, softmax_scale, out_o, out_lse, workspace,
+        stream)))
+
 
 
 def _event(e) -> _vp:
@@ -374,3 +410,38 @@ class Ring:
         if self._h is not None:
             akv_ring_destroy(self._h)
             self._h = None
+
+
+class Prepared:
+    """One library call with its arguments marshalled once.  Calling the
+    object repeats the call with the same pointers, sizes and stream, without
+    the per-call checks and conversions of the plain wrappers (a few us of
+    host time per call, which bound a step of short launches).  It holds the
+    tensors it was given, so their memory stays allocated; their contents
+    may change between calls, their shapes and storage may not."""
+
+    __slots__ = ("name", "_fn", "_args", "_keep")
+
+    def __init__(self, name: str, args: tuple, keep):
+        self.name, self._fn, self._args, self._keep = name, getattr(_lib, name), args, keep
+
+    def __call__(self):
+        _check(self.name, self._fn(*self._args))
+
+
+_PREPARABLE = {
+    "akv_decode_attn_int8": _args_decode_attn_int8,
+    "akv_decode_attn_exact": _args_decode_attn_exact,
+    "akv_decode_hybrid": _args_decode_hybrid,
+    "akv_merge_lse": _args_merge_lse,
+    "akv_decode_attn_l13": _args_decode_attn_l13,
+}
+
+
+def prepare(name: str, *args, **kwargs) -> Prepared:
+    """The call `name(*args, **kwargs)` (one of the decode entry points or
+    akv_merge_lse, same arguments as its wrapper) marshalled once, for
+    repeated launches on fixed buffers."""
+    if name not in _PREPARABLE:
+        raise ValueError(f"prepare: {name} is not one of {sorted(_PREPARABLE)}")
+    return Prepared(name, _PREPARABLE[name](*args, **kwargs), (args, kwargs))

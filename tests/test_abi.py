@@ -37,6 +37,15 @@ def test_status_strings_and_version(B):
     assert B.version().startswith("akv ")
 
 
+def test_prepare_covers_the_decode_calls_only(B):
+    """binding.prepare marshals the decode entry points and akv_merge_lse;
+    every one of them is a symbol the header declares, and other names are
+    refused before anything is called."""
+    assert set(B._PREPARABLE) <= set(B.header_functions())
+    with pytest.raises(ValueError):
+        B.prepare("akv_quantize_pages")
+
+
 def test_host_side_validation(B):
     lib = B._lib
     d = B.dims(4, 6)

@@ -509,6 +509,20 @@ def test_hybrid_step_replays_from_a_graph(B):
             assert torch.equal(o, ro) and torch.equal(l, rl), f"replay {rep} differs"
         step()  # eager work between replays
         torch.cuda.synchronize()
+    # the same calls marshalled once (binding.prepare) give the same bits
+    prepared = [B.prepare("akv_decode_hybrid", d8, 1, q, g["k_codes"], g["v_codes"], g["k_chan"], g["k_tok"],
+                          g["v_chan"], tabs[0], tabs[1], t8.shape[1], kp, vp, tabs[2], tabs[3], tw.shape[1], SIG, o,
+                          l, ws)
+                for (q, g, kp, vp), (o, l) in zip(layers, outs)]
+    for rep in range(2):
+        for o, l in outs:
+            o.fill_(float("nan"))
+            l.fill_(float("nan"))
+        for c in prepared:
+            c()
+        torch.cuda.synchronize()
+        for (o, l), (ro, rl) in zip(outs, ref):
+            assert torch.equal(o, ro) and torch.equal(l, rl), f"prepared call {rep} differs"
 
 
 # ----------------------------------------------------------------------------- fused call edge cases
