@@ -842,10 +842,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_l13_kernel(ExactArgs a, L1
 }
 
 // Both tiers of a layer in one launch: in each (request, KV head) row of the
-// grid the int8 work-groups come first and the last nw read the BF16 window
-// (measured against window-first: the same at 128K, 2 us faster per 32K step,
-// 0.8% faster batched); all write partial columns of the same rows (int8
-// columns first, window columns after them).
+// grid the first n8s work-groups are the int8 tier's and the rest read the
+// BF16 window (measured against window-first: the same at 128K, 2 us faster
+// per 32K step, 0.8% faster batched); all write partial columns of the same
+// rows (int8 columns first, window columns after them).  The leading scalar
+// arguments are the int8 tier's (see with_lead) and its column count.
 template <int PvLimbs, int Prio>
 __global__ __launch_bounds__(kThreads, 2) void decode_hybrid_kernel(const int32_t* page_table, const int32_t* n_pages,
                                                                     int max_pages, int splits, int n8s, Int8Args a8,
