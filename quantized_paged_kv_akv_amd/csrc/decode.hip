@@ -309,30 +309,42 @@ __device__ __forceinline__ void int8_split(const Int8Args& a, Int8Smem& sm, int 
     const size_t row0 = (size_t)b * Hq + (size_t)kvh * G;
 
     // Requests go out in the order they are needed: this wave's two query
-    // rows, then the first page's codes and scales; the query staging below
-    // waits only for the former and overlaps the latter.
+    // rows, its page slots, then the first page's scales and codes; the
+    // query staging below waits only for the first of them and overlaps the
+    // rest.
     const int r0 = w, r1 = w + 4;  // query rows staged by this wave
     u32x2 qraw0 = {0, 0}, qraw1 = {0, 0};
     if (r0 < G) qraw0 = *reinterpret_cast<const u32x2*>(a.q + (row0 + r0) * kD + 4 * l);
     if (r1 < G) qraw1 = *reinterpret_cast<const u32x2*>(a.q + (row0 + r1) * kD + 4 * l);
+    // No branch may surround a load from here to the first page: after a
+    // branch that issued loads the compiler waits for every outstanding load
+    // at the join, so the first page's QK would wait for all of its ring
+    // (15 us per 32K step).  Every wave therefore issues the same loads, from
+    // indices clamped into this work-group's pages.
+    //
+    // this wave's page slots (at most 64), read once; lanes past the count
+    // read the work-group's last entry
+    const int last = wg0 + len - 1;
+    const int my_slot = pt[min(pt_index(l), last)];
     u32x4 buf[16];
-    u32x4 sk0 = {0, 0, 0, 0}, sv0 = {0, 0, 0, 0};
-    float st0 = 0.0f;
-    if (cnt > 0) {
-        const int s0 = (wg0 == wg0_s) ? spec_slot : pt[pt_index(0)];  // same entry when the shares agree
+    u32x4 sk0, sv0;
+    float st0;
+    {
+        // the first page's scales, then its codes (its QK needs the scales
+        // first); a wave without pages reads the work-group's last page and
+        // ignores it
+        const int s0 = (wg0 == wg0_s && cnt > 0) ? spec_slot : pt[min(pt_index(0), last)];
         const size_t sb = (size_t)__builtin_amdgcn_readfirstlane(s0) * Hkv + kvh;
         const int8_t* kp = a.kc + sb * (kP * kD);
+        sk0 = ld16_stream(a.kchan + sb * kD + 4 * l);
+        sv0 = ld16_stream(a.vchan + sb * kD + 4 * l);
+        st0 = __builtin_nontemporal_load(a.ktok + sb * kP + l);
 #pragma unroll
         for (int s2 = 0; s2 < 4; ++s2)
 #pragma unroll
             for (int t = 0; t < 4; ++t) buf[4 * s2 + t] = ld16_stream(kp + koff + 1024 * (4 * s2 + t));
-        sk0 = ld16_stream(a.kchan + sb * kD + 4 * l);
-        sv0 = ld16_stream(a.vchan + sb * kD + 4 * l);
-        st0 = __builtin_nontemporal_load(a.ktok + sb * kP + l);
     }
-
-    // this wave's page slots, read once (the loop reads them from LDS)
-    for (int i = l; i < cnt; i += 64) sm.slot[w][i] = pt[pt_index(i)];
+    if (l < cnt) sm.slot[w][l] = my_slot;
 
     // query rows of this KV head, FP32, each scaled by 2^-e (e from its max |q|);
     // rows G..7 are zero (the MFMA columns they feed are never read)
