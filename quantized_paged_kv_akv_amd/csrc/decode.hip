@@ -39,7 +39,7 @@
 //
 // Softmax runs in base 2 (logits scaled by log2 e); LSE is returned in
 // natural log.  Each split writes a normalised partial (O, LSE) to the
-// workspace; combine_kernel folds them exactly.
+// workspace; the second pass (launch_combine) folds them exactly.
 #include <math.h>
 
 #include <mutex>

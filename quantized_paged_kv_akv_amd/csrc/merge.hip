@@ -3,8 +3,9 @@
 // valid empty partial).
 //
 // akv_merge_lse: one work-group per row (a request's query head), one thread
-// per channel.  The split-K second pass (combine_kernel) uses the same rule
-// over all of a row's split partials.
+// per channel.  The split-K second pass (launch_combine: one of four kernels
+// by the number of split columns) uses the same rule over all of a row's
+// split partials.
 #include <math.h>
 
 #include "akv_device.h"
