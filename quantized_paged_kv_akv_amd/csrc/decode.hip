@@ -768,12 +768,17 @@ __device__ __forceinline__ void exact_split(const ExactArgs& a, const Src& src, 
 #pragma unroll
     for (int j = 0; j < 4; ++j) O[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    int it = 0;
-    for (int p = p0; p < p1; ++p, ++it) {
+    // The page step; PF: load the next page first.  The last page runs
+    // outside the loop so that no load in the loop sits behind a branch:
+    // after such a branch the compiler waits for every outstanding load at
+    // the loop head, and the next page's loads no longer overlap the
+    // current page's work (all-BF16 step 1.46 against 1.50 ms at 128K, 0.47
+    // against 0.49 ms at 32K).
+    auto page = [&](auto prefetch, int p, int it) {
+        constexpr bool PF = decltype(prefetch)::value;
         if constexpr (Prio == kPrioPagesLeft) set_issue_priority(min(3, p1 - p - 1));
-        const bool has_next = p + 1 < p1;
         typename Src::Page nxt;
-        if (has_next) src.load(pt[p + 1], kvh, Hkv, w, l, nxt);
+        if constexpr (PF) src.load(pt[p + 1], kvh, Hkv, w, l, nxt);
 
         f32x4 acc[4];
 #pragma unroll
@@ -815,8 +820,12 @@ __device__ __forceinline__ void exact_split(const ExactArgs& a, const Src& src, 
             O[r >> 1] = mfma_bf16(as_bf16x8(vop), pb[r & 1], O[r >> 1]);
         });
 
-        if (has_next) cur = nxt;
-    }
+        if constexpr (PF) cur = nxt;
+    };
+    int it = 0;
+    for (int p = p0; p < p1 - 1; ++p, ++it) page(std::integral_constant<bool, true>(), p, it);
+    page(std::integral_constant<bool, false>(), p1 - 1, it);
+
 
     write_partial(O, M, lsum, valid, hi_lane, w, g, row, a.n_cols, a.col0 + split, a.part_o, a.part_lse);
 }
