@@ -255,7 +255,14 @@ struct alignas(16) Int8Smem {  // 16-byte aligned: its f32x4 rows move as 16-byt
 constexpr int kPvF16 = 0;
 constexpr int kPvI8 = 3;
 
-template <int PvLimbs, int Prio>
+// InOrder: a scheduling barrier after each PV tile keeps the products in
+// tile order.  The scheduler otherwise pulls a later value tile's product
+// next to the first one, so that point waits for 13 of the wave's 16 loads
+// in flight.  It pays when one work-group holds a CU and four waves' loads
+// in flight bound the stream (32K: 294 against 298 us per step); with two
+// work-groups per CU the scheduler's order runs faster (128K: 813 against
+// 817 us), so the launch picks by the size of the grid.
+template <int PvLimbs, int Prio, bool InOrder = false>
 __device__ __forceinline__ void int8_split(const Int8Args& a, Int8Smem& sm, int split, int kvh, int b) {
     // The wave's first page-table entry if the request fills its table row
     // (the usual single-request case), read beside the page count rather than
@@ -498,6 +505,7 @@ __device__ __forceinline__ void int8_split(const Int8Args& a, Int8Smem& sm, int 
 #pragma unroll
                 for (int r = 0; r < 4; ++r) O[j][r] = O[j][r] + vs[r] * c[r];
                 if (PF) buf[j] = ld16_stream(knp + koff + 1024 * j);  // next page's K tile
+                if constexpr (InOrder) __builtin_amdgcn_sched_barrier(0);
             }
             if (PF) {
                 float* nsc = sm.sc[w][slot ^ 1];
@@ -838,12 +846,12 @@ union SplitSmem {
     } bx;
 };
 
-template <int PvLimbs, int Prio>
+template <int PvLimbs, int Prio, bool InOrder = false>
 __global__ __launch_bounds__(kThreads, 2) void decode_int8_kernel(const int32_t* page_table, const int32_t* n_pages,
                                                                   int max_pages, int splits, Int8Args a) {
     __shared__ Int8Smem sm;
-    int8_split<PvLimbs, Prio>(with_lead(a, page_table, n_pages, max_pages, splits), sm, blockIdx.x, blockIdx.y,
-                              blockIdx.z);
+    int8_split<PvLimbs, Prio, InOrder>(with_lead(a, page_table, n_pages, max_pages, splits), sm, blockIdx.x,
+                                       blockIdx.y, blockIdx.z);
 }
 
 template <int Prio>
@@ -868,7 +876,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_l13_kernel(ExactArgs a, L1
 // per 32K step, 0.8% faster batched); all write partial columns of the same
 // rows (int8 columns first, window columns after them).  The leading scalar
 // arguments are the int8 tier's (see with_lead) and its column count.
-template <int PvLimbs, int Prio>
+template <int PvLimbs, int Prio, bool InOrder = false>
 __global__ __launch_bounds__(kThreads, 2) void decode_hybrid_kernel(const int32_t* page_table, const int32_t* n_pages,
                                                                     int max_pages, int splits, int n8s, Int8Args a8,
                                                                     ExactArgs ax) {
@@ -877,8 +885,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_hybrid_kernel(const int32_
         exact_split<Prio>(ax, Bf16Source{ax.kb, ax.vb, sm.bx.st.q[threadIdx.x >> 6]}, sm.bx.ex, blockIdx.x - n8s,
                           blockIdx.y, blockIdx.z);
     else
-        int8_split<PvLimbs, Prio>(with_lead(a8, page_table, n_pages, max_pages, splits), sm.i8, blockIdx.x, blockIdx.y,
-                                  blockIdx.z);
+        int8_split<PvLimbs, Prio, InOrder>(with_lead(a8, page_table, n_pages, max_pages, splits), sm.i8, blockIdx.x,
+                                           blockIdx.y, blockIdx.z);
 }
 
 // Tensors: non-NULL and 16-byte aligned.  int32 page tables and length
@@ -1015,6 +1023,11 @@ static void launch_split(void (*kernel)(A...), dim3 grid, hipStream_t s, A... ar
         kernel<<<grid, kThreads, 0, s>>>(args...);
 }
 
+// A grid of at most one work-group per compute unit (see InOrder).
+static bool one_per_cu(dim3 grid) {
+    return (long long)grid.x * grid.y * grid.z <= device_cu_count();
+}
+
 // The int8 kernel with its leading copies of the struct's page table, page
 // counts, row length and split count (see with_lead).
 template <typename K>
@@ -1050,7 +1063,12 @@ extern "C" akv_status akv_decode_attn_int8(const akv_dims* dims, int32_t batch, 
     split_workspace(dims, batch, plan.n_splits, workspace, &a.part_o, &a.part_lse);
     dim3 grid((unsigned)plan.n_splits, (unsigned)dims->num_kv_heads, (unsigned)batch);
     switch (pv_fp16() ? 3 + issue_priority() : issue_priority()) {
-        case 0: launch_int8(decode_int8_kernel<kPvI8, kPrioOff>, grid, s, a); break;
+        case 0:
+            if (one_per_cu(grid))
+                launch_int8(decode_int8_kernel<kPvI8, kPrioOff, true>, grid, s, a);
+            else
+                launch_int8(decode_int8_kernel<kPvI8, kPrioOff>, grid, s, a);
+            break;
         case 1: launch_int8(decode_int8_kernel<kPvI8, kPrioPagesLeft>, grid, s, a); break;
         case 2: launch_int8(decode_int8_kernel<kPvI8, kPrioWave>, grid, s, a); break;
         case 3: launch_int8(decode_int8_kernel<kPvF16, kPrioOff>, grid, s, a); break;
@@ -1149,7 +1167,12 @@ static akv_status decode_hybrid_impl(const akv_dims* dims, int32_t batch, const 
     ax.part_lse = a8.part_lse;
     dim3 grid((unsigned)n_cols, (unsigned)dims->num_kv_heads, (unsigned)batch);
     switch (pv_fp16() ? 3 + issue_priority() : issue_priority()) {
-        case 0: launch_split(decode_hybrid_kernel<kPvI8, kPrioOff>, grid, s, a8.page_table, a8.n_pages, a8.max_pages, a8.splits, n_cols - pw.n_splits, a8, ax); break;
+        case 0:
+            if (one_per_cu(grid))
+                launch_split(decode_hybrid_kernel<kPvI8, kPrioOff, true>, grid, s, a8.page_table, a8.n_pages, a8.max_pages, a8.splits, n_cols - pw.n_splits, a8, ax);
+            else
+                launch_split(decode_hybrid_kernel<kPvI8, kPrioOff>, grid, s, a8.page_table, a8.n_pages, a8.max_pages, a8.splits, n_cols - pw.n_splits, a8, ax);
+            break;
         case 1: launch_split(decode_hybrid_kernel<kPvI8, kPrioPagesLeft>, grid, s, a8.page_table, a8.n_pages, a8.max_pages, a8.splits, n_cols - pw.n_splits, a8, ax); break;
         case 2: launch_split(decode_hybrid_kernel<kPvI8, kPrioWave>, grid, s, a8.page_table, a8.n_pages, a8.max_pages, a8.splits, n_cols - pw.n_splits, a8, ax); break;
         case 3: launch_split(decode_hybrid_kernel<kPvF16, kPrioOff>, grid, s, a8.page_table, a8.n_pages, a8.max_pages, a8.splits, n_cols - pw.n_splits, a8, ax); break;
