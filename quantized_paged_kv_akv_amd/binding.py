@@ -415,8 +415,9 @@ class Ring:
 class Prepared:
     """One library call with its arguments marshalled once.  Calling the
     object repeats the call with the same pointers, sizes and stream, without
-    the per-call checks and conversions of the plain wrappers (a few us of
-    host time per call, which bound a step of short launches).  It holds the
+    the per-call checks and conversions of the plain wrappers (about 20 us
+    of host time per decode call, more than a 32K layer takes on the
+    device; a prepared call costs about 7 us).  It holds the
     tensors it was given, so their memory stays allocated; their contents
     may change between calls, their shapes and storage may not."""
 
