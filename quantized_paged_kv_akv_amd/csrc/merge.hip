@@ -320,6 +320,9 @@ akv_status launch_combine(int rows, int D, const float* part_o, const float* par
     else if (n_splits <= 16 && D == 256)
         combine_thread_kernel<16><<<dim3((unsigned)((rows + 3) / 4)), 256, 0, stream>>>(
             rows, D, n_splits, part_o, part_lse, out_o, out_lse);
+    else if (n_splits <= 16 * 4)  // 32K: 50 columns, 2-3 us less per step than with K = 8
+        combine_wave_kernel<4><<<dim3((unsigned)rows, (unsigned)(D / 64)), 256, 0, stream>>>(
+            D, n_splits, part_o, part_lse, out_o, out_lse);
     else if (n_splits <= 16 * 8)
         combine_wave_kernel<8><<<dim3((unsigned)rows, (unsigned)(D / 64)), 256, 0, stream>>>(
             D, n_splits, part_o, part_lse, out_o, out_lse);
