@@ -314,7 +314,10 @@ akv_status launch_combine(int rows, int D, const float* part_o, const float* par
                           float* out_lse, hipStream_t stream) {
     if (rows == 0) return AKV_OK;
     dim3 grid((unsigned)rows, (unsigned)(D / 32));
-    if (n_splits <= 8 && D == 256)
+    if (n_splits <= 4 && D == 256)  // the 32-request step: 4 columns, 3-4 us less per step than S = 8
+        combine_thread_kernel<4><<<dim3((unsigned)((rows + 3) / 4)), 256, 0, stream>>>(
+            rows, D, n_splits, part_o, part_lse, out_o, out_lse);
+    else if (n_splits <= 8 && D == 256)
         combine_thread_kernel<8><<<dim3((unsigned)((rows + 3) / 4)), 256, 0, stream>>>(
             rows, D, n_splits, part_o, part_lse, out_o, out_lse);
     else if (n_splits <= 16 && D == 256)

@@ -264,12 +264,12 @@ def test_exact_decode_parity(B, Hkv, G, seq_len):
     check_attn(o, lse, ro, rl, f"exact Hkv{Hkv} G{G}")
 
 
-@pytest.mark.parametrize("n_pages", [5, 8, 9, 16, 17, 64, 65, 100, 128, 129, 200, 300])
+@pytest.mark.parametrize("n_pages", [4, 5, 8, 9, 16, 17, 64, 65, 100, 128, 129, 200, 300])
 def test_split_combine_paths(B, n_pages):
     """One page per split (a launch-shape override) so the split-K second pass
     folds that many partials per row, on each side of every boundary between
-    its kernels: one thread per 4 channels folding every column (up to 8 and
-    up to 16 columns), the in-wave reductions (up to 64 and up to 128), the
+    its kernels: one thread per 4 channels folding every column (up to 4, 8
+    and 16 columns), the in-wave reductions (up to 64 and up to 128), the
     register path (up to 256) and the looping path; the last page is partial
     and one request is empty."""
     seq_len = [64 * n_pages - 17, 0]
