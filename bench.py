@@ -398,15 +398,16 @@ def run_gpu(args, w, res):
                 hyb_out=hyb_out)
 
 
-def run_config(args, w, owner_modes=False):
+def run_config(args, w, owner_modes=False, res=None):
     """A further workload at its real shape: the hybrid step (one launch per
     layer), its split kernel, and for batched workloads the same step as
     two-request (two-owner) launches and as one launch per request, plus the
-    all-BF16 step."""
+    all-BF16 step.  res: the workload's inputs, if already resident."""
     import torch
 
     device = torch.device("cuda", 0)
-    res = Resident(w, device)
+    if res is None:
+        res = Resident(w, device)
     steps = max(4, args.steps)
     # a second of untimed steps first: right after the previous workload's
     # memory is released, the first timed window of a short step reads up to
@@ -1033,6 +1034,13 @@ def main():
         return
     device = torch.device("cuda", 0)
     torch.cuda.set_device(device)
+    res32 = None
+    if w.name == "ctx128k" and not args.headline_only:
+        # the 32K inputs go into HBM first, while the allocator is fresh: built
+        # after the 128K inputs were released, the same 32K step read 3-4%
+        # slower (0.297-0.301 against 0.290 ms)
+        log("[bench] building ctx32k first")
+        res32 = Resident(configs.ctx32k(), device)
     log(f"[bench] building {w.name}: {w.layers} layers, lengths {w.lengths[:4]}...")
     res = Resident(w, device)
     r = run_gpu(args, w, res)
@@ -1109,7 +1117,7 @@ def main():
         out["extra"]["oracle_check"] = check
     if w.name == "ctx128k" and not args.headline_only:
         log("[bench] ctx32k")
-        out["extra"]["ctx32k"] = run_config(args, configs.ctx32k())
+        out["extra"]["ctx32k"] = run_config(args, configs.ctx32k(), res=res32)
         log("[bench] batched")
         out["extra"]["batched"] = run_config(args, configs.batched(), owner_modes=True)
         log("[bench] host-staged sweep 8K..128K with the tier gate's transfer model")
